@@ -1,0 +1,198 @@
+"""Benchmark: Swin3D shifted-window attention on one MI355X.
+
+One step = one call of the library over the whole stage-1 latent grid of a
+0.25-degree encoder (B=1, D=4, H=180, W=360: 259,200 tokens, 8 heads,
+head_dim 64, window (2, 6, 12), shift (1, 3, 6), bf16 I/O, -100 bias): every
+step of the path (index map, gather, masked softmax attention, scatter)
+runs inside that call. Inputs are seeded synthetic tensors already resident
+in device memory when the timed region starts.
+
+Prints one JSON line with the throughput (tokens/s), the roofline position
+of the kernel and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "window-attention tokens/s at 0.25° stage-1 shape; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
+KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wattn_bf16_stage1.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(wl):
+    """Bytes: read Q, K, V and write O once per real token. FLOPs: 4 N^2 dh per window-head."""
+    elt = 2 if wl.dtype == "bf16" else 4
+    nbytes = 4 * wl.tokens * wl.heads * wl.head_dim * elt
+    n = 1
+    for x, w in zip((wl.D, wl.H, wl.W), wl.window):
+        n *= -(-x // w)
+    n *= wl.B
+    N = wl.window[0] * wl.window[1] * wl.window[2]
+    flops = 4 * N * N * wl.head_dim * wl.heads * n
+    return nbytes, flops, n
+
+
+def kernel_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed PMC summary, if the kernel is unchanged since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256") != kernel_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle, as it stands, on whole heads of the same grid until about budget_s of work."""
+    import numpy as np
+
+    import datagen
+    import oracle
+
+    q, k, v = (datagen.full_f64(wl, t) for t in ("q", "k", "v"))
+    heads = 0
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    while heads < wl.heads:
+        sl = (Ellipsis, slice(heads, heads + 1), slice(None))
+        oracle.swin3d_window_attention(q[sl], k[sl], v[sl], wl.window, wl.shift, wl.scale, -100.0)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    token_heads = wl.tokens * heads
+    del q, k, v
+    return {
+        "value": token_heads / wl.heads / wall,
+        "unit": "tokens/s",
+        "cores": max(1, int(round(cpu / wall))),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle on the full stage-1 grid, heads 0..{heads - 1} of {wl.heads} "
+                  f"({heads * 1800} window-heads) in {wall:.1f} s; tokens/s scaled to all heads",
+        "cpu_seconds": round(cpu, 2),
+        "cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--bias", type=float, default=-100.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the attention shards by head or batch with no communication, but no multi-GPU "
+              "path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import swin3d_window_attention_amd as sw
+
+    wl = datagen.WORKLOADS["stage1"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] inputs {wl.shape} {wl.dtype}")
+    x = {t: datagen.to_torch(datagen.full_io(wl, t), wl.dtype).to(dev) for t in ("q", "k", "v")}
+    o = torch.empty_like(x["q"])
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.dtype, scale=wl.scale,
+                   cross_region_bias=args.bias)
+    info = plan.info()
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        plan.run(x["q"], x["k"], x["v"], o)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        plan.run(x["q"], x["k"], x["v"], o)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] {ms * 1000:.1f} us per step")
+
+    nbytes, flops, nwin = algorithmic_work(wl)
+    sec = ms / 1e3
+    tokens_per_s = wl.tokens / sec
+    gbs = nbytes / sec / 1e9
+    tflops = flops / sec / 1e12
+    frac_hbm = gbs / HBM_PEAK_GBS
+    frac_mfma = tflops / BF16_MFMA_PEAK_TFLOPS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) rounded to bf16)",
+        "config": {
+            "workload": "0.25-degree stage-1-like window attention",
+            "B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
+            "window": list(wl.window), "shift": list(wl.shift), "cross_region_bias": args.bias,
+            "tokens": wl.tokens, "windows": nwin, "masked_windows": info.n_masked_windows,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": frac_hbm,
+            "traffic": measured_traffic(),
+        },
+        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": frac_mfma},
+        "algorithmic_bytes_per_launch": nbytes,
+        "algorithmic_flops_per_launch": flops,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+/*
+ * swin3d_wattn.h - Swin3D shifted-window attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Flash-Aurora README, "Kernel fusion for backbone memory
+ * traffic" and "CuTe DSL window attention"; the walkthrough slides,
+ * "3 · Efficient inference"):
+ *
+ *   Q, K, V, O are grid-layout tensors [B, D, H, W, heads, head_dim],
+ *   contiguous and row-major, all of one dtype. With window w = (wd, wh, ww),
+ *   shift s and padded extents P_a = ceil(X_a / w_a) * w_a for X = (D, H, W):
+ *     1. pad D, H, W at the high end to P (padding is never read or written);
+ *     2. cyclic shift: shifted position p holds grid position (p + s) mod P;
+ *     3. partition the shifted grid into windows of N = wd*wh*ww tokens
+ *        (window (2, 6, 12) gives N = 144);
+ *     4. per window and head: S = scale * Q K^T; add cross_region_bias to S
+ *        where query and key lie in different shift regions (the Swin
+ *        shifted-window mask; the pages' value is -100, added as in PyTorch's
+ *        scaled_dot_product_attention); S = -inf for padding keys; row
+ *        softmax in FP32; O = softmax(S) V, accumulated in FP32;
+ *     5. merge the windows back, undo the shift, crop the padding.
+ *   Shift regions: along an axis with s_a > 0 the shifted grid is cut into
+ *   [0, P-w), [P-w, P-s), [P-s, P); a token's region is its triple of cuts.
+ *   A shift is applied as given, also where an axis holds a single window.
+ *
+ *   The kernels do all five steps in one pass: each workgroup gathers its
+ *   window straight from grid layout and scatters O back to grid layout;
+ *   no windowed copy and no N x N matrix ever reaches device memory.
+ *
+ * Precision: bf16 I/O uses bf16 matrix-core products for Q K^T and P V with
+ * FP32 accumulation and an FP32 softmax; P is rounded to bf16 (nearest-even)
+ * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
+ * computes everything in FP32.
+ *
+ * Ownership: the caller owns every device buffer. The library allocates no
+ * device memory; a plan is a small immutable host object.
+ *
+ * Threading: swin3d_wattn_run is asynchronous on the caller's stream and
+ * never synchronizes. One plan may be used from several host threads and
+ * streams at once.
+ *
+ * Errors: every entry point returns 0 on success or a negative code below;
+ * faults inside a kernel surface at the caller's next synchronization.
+ */
+#ifndef SWIN3D_WATTN_H
+#define SWIN3D_WATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWIN3D_WATTN_OK 0
+#define SWIN3D_WATTN_EINVAL (-1)      /* null pointer, a size <= 0, shift out of range,
+                                         non-finite scale, misaligned or overlapping buffers */
+#define SWIN3D_WATTN_EUNSUPPORTED (-2) /* valid, but no kernel for this head_dim / window / dtype */
+#define SWIN3D_WATTN_ELAUNCH (-3)     /* the HIP runtime refused the launch */
+
+typedef enum {
+  SWIN3D_WATTN_F32 = 0,  /* float32 I/O, float32 arithmetic */
+  SWIN3D_WATTN_BF16 = 1  /* bfloat16 I/O, bf16 products, float32 softmax and accumulation */
+} swin3d_wattn_dtype_t;
+
+/* Problem description, copied into the plan by swin3d_wattn_create. */
+typedef struct {
+  int32_t B, D, H, W;      /* batch and grid extents of Q/K/V/O */
+  int32_t heads, head_dim; /* innermost two dimensions */
+  int32_t window[3];       /* (wd, wh, ww), each >= 1; (2, 6, 12) in the pages */
+  int32_t shift[3];        /* 0 <= shift[a] < window[a]; (1, 3, 6) for shifted blocks */
+  int32_t dtype;           /* swin3d_wattn_dtype_t */
+  float scale;             /* > 0 and finite; normally 1/sqrt(head_dim) */
+  float cross_region_bias; /* added to S across shift regions: -100 (pages) or -INFINITY
+                              (exclusion); must be <= 0 and not NaN */
+} swin3d_wattn_desc_t;
+
+typedef struct swin3d_wattn_plan* swin3d_wattn_t;
+
+/* Validate *desc and build a plan. Host-only: no device is touched.
+ * Supported: dtype BF16 with head_dim 64 and wd*wh*ww = 144; dtype F32 with
+ * head_dim 32 or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31.
+ * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
+ * (then *out is set to NULL when out is not NULL). */
+int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
+
+/* O = window_attention(Q, K, V) on `stream` (a hipStream_t; NULL is the
+ * default stream) for the device current on the calling thread.
+ * q, k, v, o: device pointers to B*D*H*W*heads*head_dim elements of the
+ * plan's dtype, 16-byte aligned; o must not overlap q, k or v (q, k, v may
+ * alias each other). Every element of o is written exactly once.
+ * Returns 0, EINVAL (null plan or pointer, misalignment, overlap) or ELAUNCH. */
+int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* k, const void* v, void* o,
+                     void* stream);
+
+/* Release a plan. NULL is a no-op. Returns 0. */
+int swin3d_wattn_destroy(swin3d_wattn_t plan);
+
+/* Static English text for a return code. */
+const char* swin3d_wattn_strerror(int code);
+
+/* Geometry of a plan, for callers that size work or report throughput. */
+typedef struct {
+  int32_t padded[3];        /* P = (PD, PH, PW) */
+  int32_t windows_per_axis[3];
+  int64_t n_windows;        /* B * prod(windows_per_axis): the folded batch of the pages */
+  int64_t n_masked_windows; /* windows that hold more than one shift region or padding */
+  int32_t tokens_per_window;/* N */
+  int64_t tokens;           /* B*D*H*W real tokens */
+  int64_t workgroups;       /* workgroups one run launches */
+  int32_t threads_per_workgroup;
+  int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel */
+} swin3d_wattn_info_t;
+
+/* Fill *info for a plan. Host-only. Returns 0 or EINVAL. */
+int swin3d_wattn_get_info(swin3d_wattn_t plan, swin3d_wattn_info_t* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIN3D_WATTN_H */

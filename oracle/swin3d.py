@@ -198,27 +198,18 @@ def window_slot_coords(grid, window, shift, win):
 def windows_attention(fetch, B, grid, heads, dh, window, shift, scale, bias, windows):
     """Attention outputs of the listed windows.
 
-    fetch(tensor, b, d) returns the float64 slice [H, W, heads, dh] of tensor
-    'q', 'k' or 'v' at batch b, depth d. windows: iterable of (b, kd, kh, kw).
+    fetch(tensor, b, coords) returns the float64 rows [n, heads, dh] of tensor
+    'q', 'k' or 'v' at batch b and grid coordinates coords [n, 3].
+    windows: iterable of (b, kd, kh, kw).
     Returns a list of (b, coords [n, 3], O [n, heads, dh]) over real slots."""
     out = []
-    cache = {}
-
-    def get(t, b, d):
-        key = (t, b, d)
-        if key not in cache:
-            cache[key] = fetch(t, b, d)
-        return cache[key]
-
     for (b, kd, kh, kw) in windows:
         g, valid, labels = window_slot_coords(grid, window, shift, (kd, kh, kw))
         n = g.shape[0]
         gath = {}
         for t in ("q", "k", "v"):
             a = np.zeros((n, heads, dh), dtype=np.float64)
-            for i in range(n):
-                if valid[i]:
-                    a[i] = get(t, b, int(g[i, 0]))[g[i, 1], g[i, 2]]
+            a[valid] = fetch(t, b, g[valid])
             gath[t] = a
         o, _, _ = masked_window_attention(gath["q"][None], gath["k"][None], gath["v"][None],
                                           labels[None], valid[None], scale, bias)

@@ -1,0 +1,211 @@
+"""Python binding of libswin3d_wattn (Swin3D shifted-window attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the shared library. PyTorch is used for device memory and the
+current stream. There is no CPU fallback: if the library is missing, every
+call raises.
+
+The C entry points are exposed under their own names
+(swin3d_wattn_create / _run / _destroy / _strerror / _get_info) plus a small
+convenience layer (Plan, window_attention).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "SWIN3D_WATTN_OK", "SWIN3D_WATTN_EINVAL", "SWIN3D_WATTN_EUNSUPPORTED", "SWIN3D_WATTN_ELAUNCH",
+    "SWIN3D_WATTN_F32", "SWIN3D_WATTN_BF16", "Swin3dWattnDesc", "Swin3dWattnInfo", "Swin3dWattnError",
+    "lib_path", "load_library", "swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_destroy",
+    "swin3d_wattn_strerror", "swin3d_wattn_get_info", "Plan", "window_attention",
+]
+
+SWIN3D_WATTN_OK = 0
+SWIN3D_WATTN_EINVAL = -1
+SWIN3D_WATTN_EUNSUPPORTED = -2
+SWIN3D_WATTN_ELAUNCH = -3
+SWIN3D_WATTN_F32 = 0
+SWIN3D_WATTN_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libswin3d_wattn.so"
+
+
+class Swin3dWattnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("D", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("cross_region_bias", ctypes.c_float),
+    ]
+
+
+class Swin3dWattnInfo(ctypes.Structure):
+    _fields_ = [
+        ("padded", ctypes.c_int32 * 3), ("windows_per_axis", ctypes.c_int32 * 3),
+        ("n_windows", ctypes.c_int64), ("n_masked_windows", ctypes.c_int64),
+        ("tokens_per_window", ctypes.c_int32), ("tokens", ctypes.c_int64),
+        ("workgroups", ctypes.c_int64), ("threads_per_workgroup", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+    ]
+
+
+class Swin3dWattnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {swin3d_wattn_strerror(code)} ({code})")
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library():
+    """Load the in-tree shared library (built by swin3d_window_attention_amd.build)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m swin3d_window_attention_amd.build`")
+        lib = ctypes.CDLL(path)
+        lib.swin3d_wattn_create.argtypes = [ctypes.POINTER(Swin3dWattnDesc), ctypes.POINTER(ctypes.c_void_p)]
+        lib.swin3d_wattn_create.restype = ctypes.c_int
+        lib.swin3d_wattn_run.argtypes = [ctypes.c_void_p] * 6
+        lib.swin3d_wattn_run.restype = ctypes.c_int
+        lib.swin3d_wattn_destroy.argtypes = [ctypes.c_void_p]
+        lib.swin3d_wattn_destroy.restype = ctypes.c_int
+        lib.swin3d_wattn_strerror.argtypes = [ctypes.c_int]
+        lib.swin3d_wattn_strerror.restype = ctypes.c_char_p
+        lib.swin3d_wattn_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(Swin3dWattnInfo)]
+        lib.swin3d_wattn_get_info.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+# ---- the C entry points, same names -------------------------------------
+
+def swin3d_wattn_create(desc: Swin3dWattnDesc):
+    """Returns (code, plan handle or None)."""
+    h = ctypes.c_void_p()
+    rc = load_library().swin3d_wattn_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, (h.value if rc == 0 else None)
+
+
+def swin3d_wattn_run(plan, q: int, k: int, v: int, o: int, stream: int = 0) -> int:
+    return load_library().swin3d_wattn_run(plan, q, k, v, o, stream)
+
+
+def swin3d_wattn_destroy(plan) -> int:
+    return load_library().swin3d_wattn_destroy(plan)
+
+
+def swin3d_wattn_strerror(code: int) -> str:
+    return load_library().swin3d_wattn_strerror(code).decode()
+
+
+def swin3d_wattn_get_info(plan):
+    info = Swin3dWattnInfo()
+    rc = load_library().swin3d_wattn_get_info(plan, ctypes.byref(info))
+    return rc, info
+
+
+# ---- convenience layer --------------------------------------------------
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    if dtype in (torch.float32, "f32", "float32"):
+        return SWIN3D_WATTN_F32
+    if dtype in (torch.bfloat16, "bf16", "bfloat16"):
+        return SWIN3D_WATTN_BF16
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def make_desc(B, D, H, W, heads, head_dim, window=(2, 6, 12), shift=(0, 0, 0), dtype="bf16",
+              scale=None, cross_region_bias=-100.0) -> Swin3dWattnDesc:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    d = Swin3dWattnDesc()
+    d.B, d.D, d.H, d.W, d.heads, d.head_dim = B, D, H, W, heads, head_dim
+    d.window = (ctypes.c_int32 * 3)(*window)
+    d.shift = (ctypes.c_int32 * 3)(*shift)
+    d.dtype = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    d.scale = scale
+    d.cross_region_bias = cross_region_bias
+    return d
+
+
+class Plan:
+    """An immutable plan for one problem shape; run() launches on the current stream."""
+
+    def __init__(self, B, D, H, W, heads, head_dim, window=(2, 6, 12), shift=(0, 0, 0), dtype="bf16",
+                 scale=None, cross_region_bias=-100.0):
+        self.desc = make_desc(B, D, H, W, heads, head_dim, window, shift, dtype, scale, cross_region_bias)
+        self.shape = (B, D, H, W, heads, head_dim)
+        rc, h = swin3d_wattn_create(self.desc)
+        if rc != SWIN3D_WATTN_OK:
+            raise Swin3dWattnError(rc, "swin3d_wattn_create")
+        self._h = h
+        self._lib = load_library()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> Swin3dWattnInfo:
+        rc, info = swin3d_wattn_get_info(self._h)
+        if rc != SWIN3D_WATTN_OK:
+            raise Swin3dWattnError(rc, "swin3d_wattn_get_info")
+        return info
+
+    def run(self, q, k, v, o, stream=None) -> None:
+        import torch
+
+        for t in (q, k, v, o):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("q, k, v, o must be contiguous device tensors")
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"expected shape {self.shape}, got {tuple(t.shape)}")
+            if _dtype_code(t.dtype) != self.desc.dtype:
+                raise ValueError("tensor dtype does not match the plan")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        rc = self._lib.swin3d_wattn_run(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        stream)
+        if rc != SWIN3D_WATTN_OK:
+            raise Swin3dWattnError(rc, "swin3d_wattn_run")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            swin3d_wattn_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def window_attention(q, k, v, window=(2, 6, 12), shift=(0, 0, 0), scale=None, cross_region_bias=-100.0,
+                     out=None):
+    """Swin3D shifted-window attention of grid-layout device tensors [B, D, H, W, heads, head_dim]."""
+    import torch
+
+    B, D, H, W, heads, dh = q.shape
+    plan = Plan(B, D, H, W, heads, dh, window, shift, q.dtype, scale, cross_region_bias)
+    if out is None:
+        out = torch.empty_like(q)
+    plan.run(q, k, v, out)
+    return out

@@ -1,0 +1,177 @@
+// Host side of the C ABI: argument checks and plan geometry. Nothing here
+// touches a device, so plans can be built and validated without a GPU.
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "plan.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-axis flags of each window index along one axis: `cut` when the window
+// holds two shift regions (the last window along a shifted axis), `pad` when
+// one of its positions maps to padding. Shifted position p holds grid
+// position (p + s) mod P, so the padding lands at p in [X - s, P - s), which
+// need not be the last window; hence the scan.
+void axis_flags(int32_t X, int32_t w, int32_t s, int32_t P, int32_t n, bool* cut, bool* pad) {
+  for (int32_t kw = 0; kw < n; ++kw) {
+    cut[kw] = (s > 0) && (kw == n - 1);
+    bool any_pad = false;
+    for (int32_t o = 0; o < w; ++o) {
+      int32_t p = kw * w + o;
+      int32_t g = p + s;
+      if (g >= P) g -= P;
+      if (g >= X) any_pad = true;
+    }
+    pad[kw] = any_pad;
+  }
+}
+
+bool bad_dim(int32_t v) { return v <= 0; }
+
+}  // namespace
+
+extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out) {
+  if (out) *out = nullptr;
+  if (!desc || !out) return SWIN3D_WATTN_EINVAL;
+  const swin3d_wattn_desc_t& d = *desc;
+  if (bad_dim(d.B) || bad_dim(d.D) || bad_dim(d.H) || bad_dim(d.W) || bad_dim(d.heads) ||
+      bad_dim(d.head_dim))
+    return SWIN3D_WATTN_EINVAL;
+  for (int a = 0; a < 3; ++a) {
+    if (d.window[a] <= 0) return SWIN3D_WATTN_EINVAL;
+    if (d.shift[a] < 0 || d.shift[a] >= d.window[a]) return SWIN3D_WATTN_EINVAL;
+  }
+  if (d.dtype != SWIN3D_WATTN_F32 && d.dtype != SWIN3D_WATTN_BF16) return SWIN3D_WATTN_EINVAL;
+  if (!std::isfinite(d.scale) || !(d.scale > 0.0f)) return SWIN3D_WATTN_EINVAL;
+  if (std::isnan(d.cross_region_bias) || d.cross_region_bias > 0.0f) return SWIN3D_WATTN_EINVAL;
+
+  const int32_t X[3] = {d.D, d.H, d.W};
+  int64_t tokens = (int64_t)d.B * d.D * d.H * d.W;
+  if (tokens >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+  int64_t padded_tokens = d.B;
+  int32_t P[3], nwin[3];
+  for (int a = 0; a < 3; ++a) {
+    int64_t pa = ceil_div(X[a], d.window[a]) * d.window[a];
+    if (pa >= (int64_t(1) << 30)) return SWIN3D_WATTN_EUNSUPPORTED;
+    P[a] = (int32_t)pa;
+    nwin[a] = (int32_t)(pa / d.window[a]);
+    padded_tokens *= pa;
+  }
+  if (padded_tokens >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+  const int64_t N64 = (int64_t)d.window[0] * d.window[1] * d.window[2];
+  if (N64 > 4096) return SWIN3D_WATTN_EUNSUPPORTED;
+  const int32_t N = (int32_t)N64;
+
+  int32_t kernel = -1, threads = 0;
+  if (d.dtype == SWIN3D_WATTN_BF16) {
+    if (d.head_dim == 64 && N == 144) { kernel = 1; threads = 192; }
+  } else {
+    if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
+      kernel = 0;
+      threads = (int32_t)(ceil_div(N, 64) * 64);
+    }
+  }
+  if (kernel < 0) return SWIN3D_WATTN_EUNSUPPORTED;
+
+  int64_t elems = tokens * d.heads * d.head_dim;
+  int64_t n_windows = (int64_t)d.B * nwin[0] * nwin[1] * nwin[2];
+  int64_t workgroups = n_windows * d.heads;
+  if (workgroups >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+
+  // masked-window count (windows needing the region / padding path)
+  int64_t masked = 0;
+  {
+    bool* flags[3][2];
+    for (int a = 0; a < 3; ++a) {
+      flags[a][0] = new (std::nothrow) bool[nwin[a]];
+      flags[a][1] = new (std::nothrow) bool[nwin[a]];
+      if (!flags[a][0] || !flags[a][1]) {
+        for (int b = 0; b <= a; ++b) { delete[] flags[b][0]; delete[] flags[b][1]; }
+        return SWIN3D_WATTN_EINVAL;
+      }
+      axis_flags(X[a], d.window[a], d.shift[a], P[a], nwin[a], flags[a][0], flags[a][1]);
+    }
+    // a window needs the mask path if any axis is cut or padded
+    int64_t plain[3];
+    for (int a = 0; a < 3; ++a) {
+      plain[a] = 0;
+      for (int32_t i = 0; i < nwin[a]; ++i)
+        if (!flags[a][0][i] && !flags[a][1][i]) ++plain[a];
+    }
+    masked = n_windows - (int64_t)d.B * plain[0] * plain[1] * plain[2];
+    for (int a = 0; a < 3; ++a) { delete[] flags[a][0]; delete[] flags[a][1]; }
+  }
+
+  swin3d_wattn_plan* p = new (std::nothrow) swin3d_wattn_plan;
+  if (!p) return SWIN3D_WATTN_EINVAL;
+  p->desc = d;
+  for (int a = 0; a < 3; ++a) { p->padded[a] = P[a]; p->nwin[a] = nwin[a]; }
+  p->n_windows = n_windows;
+  p->n_masked_windows = masked;
+  p->N = N;
+  p->tokens = tokens;
+  p->elems = elems;
+  p->elem_bytes = d.dtype == SWIN3D_WATTN_BF16 ? 2 : 4;
+  p->kernel = kernel;
+  p->workgroups = workgroups;
+  p->threads = threads;
+  p->c2 = (float)((double)d.scale * kLog2e);
+  p->bias2 = std::isinf(d.cross_region_bias) ? -INFINITY
+                                             : (float)((double)d.cross_region_bias * kLog2e);
+  *out = p;
+  return SWIN3D_WATTN_OK;
+}
+
+extern "C" int swin3d_wattn_destroy(swin3d_wattn_t plan) {
+  delete plan;
+  return SWIN3D_WATTN_OK;
+}
+
+extern "C" const char* swin3d_wattn_strerror(int code) {
+  switch (code) {
+    case SWIN3D_WATTN_OK: return "success";
+    case SWIN3D_WATTN_EINVAL: return "invalid argument";
+    case SWIN3D_WATTN_EUNSUPPORTED: return "unsupported head_dim, window, dtype or size";
+    case SWIN3D_WATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int swin3d_wattn_get_info(swin3d_wattn_t plan, swin3d_wattn_info_t* info) {
+  if (!plan || !info) return SWIN3D_WATTN_EINVAL;
+  for (int a = 0; a < 3; ++a) {
+    info->padded[a] = plan->padded[a];
+    info->windows_per_axis[a] = plan->nwin[a];
+  }
+  info->n_windows = plan->n_windows;
+  info->n_masked_windows = plan->n_masked_windows;
+  info->tokens_per_window = plan->N;
+  info->tokens = plan->tokens;
+  info->workgroups = plan->workgroups;
+  info->threads_per_workgroup = plan->threads;
+  info->kernel = plan->kernel;
+  return SWIN3D_WATTN_OK;
+}
+
+namespace {
+bool overlaps(const void* a, const void* b, int64_t bytes) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+}
+bool misaligned(const void* a) { return ((uintptr_t)a & 15u) != 0; }
+}  // namespace
+
+extern "C" int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* k, const void* v,
+                                void* o, void* stream) {
+  if (!plan || !q || !k || !v || !o) return SWIN3D_WATTN_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return SWIN3D_WATTN_EINVAL;
+  const int64_t bytes = plan->elems * plan->elem_bytes;
+  if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
+    return SWIN3D_WATTN_EINVAL;
+  return swin3d_wattn_launch(plan, q, k, v, o, stream);
+}

@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+validates arguments. No call here reaches a device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import datagen
+import oracle
+import swin3d_window_attention_amd as sw
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swin3d_wattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(swin3d_wattn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sw.load_library()
+    names = _declared_functions()
+    assert names == sorted(["swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_destroy",
+                            "swin3d_wattn_strerror", "swin3d_wattn_get_info"])
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(sw, n), n  # the binding uses the same names
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("SWIN3D_WATTN_OK", "SWIN3D_WATTN_EINVAL", "SWIN3D_WATTN_EUNSUPPORTED", "SWIN3D_WATTN_ELAUNCH"):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(sw, name)
+    assert ctypes.sizeof(sw.Swin3dWattnDesc) == 4 * 15
+
+
+def _create(**kw):
+    base = dict(B=1, D=4, H=180, W=360, heads=8, head_dim=64, window=(2, 6, 12), shift=(1, 3, 6),
+                dtype="bf16", scale=0.125, cross_region_bias=-100.0)
+    base.update(kw)
+    return sw.swin3d_wattn_create(sw.make_desc(**base))
+
+
+def test_create_ok_and_info_matches_pages():
+    for name, masked in [("stage1", 959), ("stage2", 254), ("stage2_s0", 0), ("stage3_pad", 79),
+                         ("tiny_f32", 4), ("stress_hres", 11548)]:
+        wl = datagen.WORKLOADS[name]
+        rc, h = _create(B=wl.B, D=wl.D, H=wl.H, W=wl.W, heads=wl.heads, head_dim=wl.head_dim,
+                        shift=wl.shift, dtype=wl.dtype, scale=wl.scale)
+        assert rc == 0 and h
+        rc, info = sw.swin3d_wattn_get_info(h)
+        assert rc == 0
+        assert info.n_windows == oracle.window_count(wl.B, (wl.D, wl.H, wl.W), wl.window)
+        assert info.n_masked_windows == masked
+        assert info.tokens_per_window == 144
+        assert info.tokens == wl.tokens
+        assert list(info.padded) == [oracle.padded_extent(x, w) for x, w in zip((wl.D, wl.H, wl.W), wl.window)]
+        assert info.workgroups == info.n_windows * wl.heads
+        assert sw.swin3d_wattn_destroy(h) == 0
+
+
+def test_masked_window_count_matches_oracle_labels():
+    """The plan's count of windows needing the mask path equals the windows whose
+    oracle labels or validity are not uniform."""
+    for grid, shift in [((4, 45, 90), (1, 3, 6)), ((3, 7, 13), (1, 5, 11)), ((4, 44, 30), (1, 3, 6)),
+                        ((2, 12, 24), (0, 0, 0)), ((4, 18, 36), (0, 3, 0))]:
+        rc, h = _create(D=grid[0], H=grid[1], W=grid[2], shift=shift, dtype="f32", head_dim=32)
+        assert rc == 0
+        _, info = sw.swin3d_wattn_get_info(h)
+        padded = tuple(oracle.padded_extent(x, w) for x, w in zip(grid, (2, 6, 12)))
+        import numpy as np
+        lab = oracle.window_partition(oracle.region_labels(padded, (2, 6, 12), shift)[None], (2, 6, 12))
+        val = oracle.window_partition(oracle.cyclic_shift(
+            oracle.pad_to_windows(np.ones((1,) + grid, bool), (2, 6, 12), False), shift), (2, 6, 12))
+        expected = sum(1 for w in range(lab.shape[0]) if len(np.unique(lab[w])) > 1 or not val[w].all())
+        assert info.n_masked_windows == expected, (grid, shift)
+        sw.swin3d_wattn_destroy(h)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(D=-1), -1), (dict(heads=0), -1), (dict(head_dim=0), -1),
+    (dict(window=(0, 6, 12)), -1), (dict(shift=(2, 3, 6)), -1), (dict(shift=(-1, 0, 0)), -1),
+    (dict(shift=(1, 6, 6)), -1), (dict(dtype=7), -1), (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
+    (dict(cross_region_bias=float("nan")), -1), (dict(cross_region_bias=1.0), -1),
+    (dict(head_dim=128), -2), (dict(head_dim=32), -2), (dict(window=(2, 6, 6), shift=(1, 3, 3)), -2), (dict(window=(2, 6, 6)), -1),
+    (dict(window=(4, 8, 12), shift=(1, 3, 3), dtype="f32", head_dim=64), -2),
+    (dict(dtype="f32", head_dim=48), -2),
+    (dict(B=2, D=4, H=46341, W=46341), -2),
+])
+def test_create_rejects(kw, code):
+    rc, h = _create(**kw)
+    assert rc == code and h is None
+
+
+def test_create_accepts_edge_cases():
+    for kw in [dict(cross_region_bias=-math.inf), dict(shift=(0, 0, 0)), dict(shift=(1, 5, 11)),
+               dict(D=1, H=1, W=1), dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)),
+               dict(dtype="f32", head_dim=64, window=(4, 8, 8), shift=(3, 7, 7))]:
+        rc, h = _create(**kw)
+        assert rc == 0, kw
+        sw.swin3d_wattn_destroy(h)
+
+
+def test_null_arguments():
+    lib = sw.load_library()
+    assert lib.swin3d_wattn_create(None, None) == -1
+    out = ctypes.c_void_p(123)
+    assert lib.swin3d_wattn_create(None, ctypes.byref(out)) == -1
+    assert out.value is None
+    assert sw.swin3d_wattn_destroy(None) == 0
+    assert sw.swin3d_wattn_get_info(None)[0] == -1
+    assert sw.swin3d_wattn_run(None, 16, 32, 48, 64, 0) == -1
+
+
+def test_run_rejects_bad_pointers_before_launch():
+    """Misaligned, null or overlapping buffers are refused on the host: nothing is launched."""
+    rc, h = _create(B=1, D=2, H=6, W=12, heads=1)
+    assert rc == 0
+    n = 2 * 6 * 12 * 64 * 2
+    base = 1 << 40
+    q, k, v, o = base, base + 4 * n, base + 8 * n, base + 12 * n
+    assert sw.swin3d_wattn_run(h, q + 2, k, v, o, 0) == -1   # misaligned
+    assert sw.swin3d_wattn_run(h, q, k, v, o + 8, 0) == -1   # misaligned
+    assert sw.swin3d_wattn_run(h, 0, k, v, o, 0) == -1       # null
+    assert sw.swin3d_wattn_run(h, q, k, v, q + 16, 0) == -1  # o overlaps q
+    assert sw.swin3d_wattn_run(h, q, k, v, v - n + 16, 0) == -1  # o overlaps v
+    sw.swin3d_wattn_destroy(h)
+
+
+def test_strerror():
+    assert sw.swin3d_wattn_strerror(0) == "success"
+    for c in (-1, -2, -3):
+        assert sw.swin3d_wattn_strerror(c) and sw.swin3d_wattn_strerror(c) != "success"
+    assert "unknown" in sw.swin3d_wattn_strerror(42)

@@ -283,7 +283,8 @@ def test_windows_attention_matches_full(grid, shift, bias):
     arrays = {"q": q, "k": k, "v": v}
     nwin = [oracle.padded_extent(x, w) // w for x, w in zip(grid, WIN)]
     wins = [(b, a, c, e) for b in range(B) for a in range(nwin[0]) for c in range(nwin[1]) for e in range(nwin[2])]
-    res = oracle.windows_attention(lambda t, b, d: arrays[t][b, d], B, grid, h, dh, WIN, shift, 0.5, bias, wins)
+    fetch = lambda t, b, c: arrays[t][b, c[:, 0], c[:, 1], c[:, 2]]
+    res = oracle.windows_attention(fetch, B, grid, h, dh, WIN, shift, 0.5, bias, wins)
     seen = 0
     for b, coords, ow in res:
         np.testing.assert_allclose(ow, o[b, coords[:, 0], coords[:, 1], coords[:, 2]], rtol=0, atol=1e-13)
