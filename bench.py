@@ -66,37 +66,55 @@ def measured_traffic():
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The fp64 oracle, as it stands, on whole heads of the same grid until about budget_s of work."""
-    import numpy as np
-
+    """The fp64 oracle, as it stands, run head by head over the same grid (cycling through the
+    heads again if needed) until about budget_s of wall time has been spent."""
     import datagen
     import oracle
 
     q, k, v = (datagen.full_f64(wl, t) for t in ("q", "k", "v"))
-    heads = 0
+    done = 0
     r0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    while heads < wl.heads:
-        sl = (Ellipsis, slice(heads, heads + 1), slice(None))
+    while True:
+        h = done % wl.heads
+        sl = (Ellipsis, slice(h, h + 1), slice(None))
         oracle.swin3d_window_attention(q[sl], k[sl], v[sl], wl.window, wl.shift, wl.scale, -100.0)
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= wl.heads // 2:
             break
     wall = time.perf_counter() - t0
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
-    token_heads = wl.tokens * heads
     del q, k, v
     return {
-        "value": token_heads / wl.heads / wall,
+        "value": wl.tokens * done / wl.heads / wall,
         "unit": "tokens/s",
         "cores": max(1, int(round(cpu / wall))),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle on the full stage-1 grid, heads 0..{heads - 1} of {wl.heads} "
-                  f"({heads * 1800} window-heads) in {wall:.1f} s; tokens/s scaled to all heads",
+        "sample": f"fp64 numpy oracle on the full stage-1 grid, one head per call, {done} head passes "
+                  f"({done * 1800} window-heads = {done / wl.heads:.2f} x the workload) in {wall:.1f} s",
         "cpu_seconds": round(cpu, 2),
         "cores_available": len(os.sched_getaffinity(0)),
     }
+
+
+def copy_calibration(nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters of a profiler."""
+    import torch
+
+    n = nbytes // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n * 2, "copy_bytes_written": n * 2, "steps": steps,
+                      "gbs_read_plus_write": 2 * n * 2 / dt / 1e9}), flush=True)
 
 
 def main():
@@ -107,6 +125,8 @@ def main():
     ap.add_argument("--bias", type=float, default=-100.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (profiler counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -114,6 +134,10 @@ def main():
               "the attention shards by head or batch with no communication, but no multi-GPU "
               "path is built", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import torch
 

@@ -2,6 +2,7 @@
 // touches a device, so plans can be built and validated without a GPU.
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <new>
 
 #include "plan.h"
@@ -32,6 +33,21 @@ void axis_flags(int32_t X, int32_t w, int32_t s, int32_t P, int32_t n, bool* cut
 }
 
 bool bad_dim(int32_t v) { return v <= 0; }
+
+uint16_t bf16_rne(double x) {
+  float f = (float)x;
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+double bf16_value(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
 
 }  // namespace
 
@@ -69,7 +85,7 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   int32_t kernel = -1, threads = 0;
   if (d.dtype == SWIN3D_WATTN_BF16) {
-    if (d.head_dim == 64 && N == 144) { kernel = 1; threads = 192; }
+    if (d.head_dim == 64 && N == 144) { kernel = 1; threads = 256; }
   } else {
     if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
       kernel = 0;
@@ -85,6 +101,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   // masked-window count (windows needing the region / padding path)
   int64_t masked = 0;
+  int32_t special[3][3];
+  bool bad_special = false;
   {
     bool* flags[3][2];
     for (int a = 0; a < 3; ++a) {
@@ -100,15 +118,27 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     int64_t plain[3];
     for (int a = 0; a < 3; ++a) {
       plain[a] = 0;
-      for (int32_t i = 0; i < nwin[a]; ++i)
-        if (!flags[a][0][i] && !flags[a][1][i]) ++plain[a];
+      int ns = 0;
+      for (int j = 0; j < 3; ++j) special[a][j] = -1;
+      for (int32_t i = 0; i < nwin[a]; ++i) {
+        if (!flags[a][0][i] && !flags[a][1][i]) {
+          ++plain[a];
+        } else if (ns < 3) {
+          special[a][ns++] = i;
+        } else {
+          bad_special = true;  // cannot happen: padding spans < one window, plus the last window
+        }
+      }
     }
     masked = n_windows - (int64_t)d.B * plain[0] * plain[1] * plain[2];
     for (int a = 0; a < 3; ++a) { delete[] flags[a][0]; delete[] flags[a][1]; }
   }
 
+  if (bad_special) return SWIN3D_WATTN_EUNSUPPORTED;
+
   swin3d_wattn_plan* p = new (std::nothrow) swin3d_wattn_plan;
   if (!p) return SWIN3D_WATTN_EINVAL;
+  std::memset(p, 0, sizeof(*p));
   p->desc = d;
   for (int a = 0; a < 3; ++a) { p->padded[a] = P[a]; p->nwin[a] = nwin[a]; }
   p->n_windows = n_windows;
@@ -123,6 +153,25 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   p->c2 = (float)((double)d.scale * kLog2e);
   p->bias2 = std::isinf(d.cross_region_bias) ? -INFINITY
                                              : (float)((double)d.cross_region_bias * kLog2e);
+  p->n_items = n_windows * d.heads;
+  // bias / scale as three bf16 terms (exact to ~2^-24 relative); anything at or
+  // beyond -2^100 excludes, like -inf: its exponential is exactly zero
+  const double big = -0x1p100;
+  double bp = std::isinf(d.cross_region_bias) ? big : (double)d.cross_region_bias / (double)d.scale;
+  if (bp < big) bp = big;
+  double rest = bp;
+  for (int t = 0; t < 3; ++t) {
+    p->beta_bf16[t] = bf16_rne(rest);
+    rest -= bf16_value(p->beta_bf16[t]);
+  }
+  p->pad_bf16 = bf16_rne(big);
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < 3; ++j) p->special[a][j] = special[a][j];
+  for (int32_t n = 0; n < N && n < 256; ++n) {
+    const int32_t whw = d.window[1] * d.window[2];
+    const int32_t od = n / whw, oh = (n % whw) / d.window[2], ow = n % d.window[2];
+    p->slot[n] = (uint32_t)od | ((uint32_t)oh << 8) | ((uint32_t)ow << 16);
+  }
   *out = p;
   return SWIN3D_WATTN_OK;
 }

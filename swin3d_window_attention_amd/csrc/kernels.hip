@@ -184,21 +184,35 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// BF16 path: matrix-core kernel for N = 144 (window (2, 6, 12)), head_dim 64.
+// BF16 path: persistent matrix-core kernel for N = 144 tokens per window
+// (window (2, 6, 12) or any other with 144 slots), head_dim 64.
 //
-// Orientation. The kernel computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
-// (A = 16 keys x 32 dims from LDS, B = 32 dims x 16 queries from registers).
-// Its accumulator gives each lane four keys of one query, which is exactly
-// the layout the B operand of the next product wants, so O^T = V^T P^T runs
-// from registers with no LDS round trip for P: for key step j the lane packs
-// keys {32j + 4g + i} and {32j + 16 + 4g + i} (g = lane / 16, i = 0..3), and
-// reads V^T with the same key assignment. The 144 keys are four 32-key
-// steps plus one 16-key step (v_mfma_f32_16x16x16_bf16).
+// Work: items are (window, head) pairs, item = window * heads + head; each
+// workgroup owns a contiguous range of items, so the index map, the region
+// codes and the mask features are rebuilt only when its window changes.
+// While it computes one item, each thread already holds the next item's
+// Q, K, V rows in registers (global loads in flight), so HBM latency hides
+// behind the matrix and softmax work.
 //
-// Work split: 3 waves x 3 query tiles of 16 rows = 144 queries.
-// LDS: K row-major [144][72] (64 + 8 pad), V^T [64][152] (144 + 8 pad),
-// slot table (token index, region code). The softmax is FP32 in the log2
-// domain: t = S * scale * log2(e) + bias * log2(e), p = 2^(t - max t).
+// LDS per item: Q, K, V row-major (128 B rows, 16-byte chunks XOR-swizzled
+// by row bits 1..3 so the operand reads below hit 16 distinct bank groups);
+// per window: the mask features of K, the region code and token of each slot.
+// Row sums of P come from the matrix core too: a fifth accumulator whose A
+// operand is all ones, so the normaliser sums the same bf16 P as the output.
+//
+// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims, B = 32
+// dims x 16 queries). Its accumulator gives each lane four keys of one
+// query, which is the B-operand layout of O^T = V^T P^T, so P never leaves
+// registers. The V^T operand is read straight from row-major V with
+// ds_read_b64_tr_b16: within each 16-lane group, input lane 4e + q points at
+// 4 dims of key e and output lane m receives key e of dim 4(m/4) + m%4.
+//
+// Mask on the matrix core: a third k-step of 32 extra "dims" adds the
+// shifted-window bias. Q gets a one-hot of its region in each of three
+// 8-wide slots (plus a constant 1 in a pad column); K gets bias/scale
+// (split into three bf16 terms) at every region other than its own, and
+// -2^100 in the pad column when it is padding. The product adds exactly the
+// bias where regions differ and pushes padding keys to a zero weight.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short short4_t __attribute__((__vector_size__(8)));
@@ -210,30 +224,45 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 // Matrix-core ordering. An MFMA whose accumulator input comes from one of
 // the last few MFMAs waits inside the matrix pipeline after issue and reads
 // its A/B registers late; an LDS load issued behind it can overwrite them
-// first. The kernels therefore interleave independent accumulators and pin
+// first. The kernel therefore interleaves independent accumulators and pins
 // the MFMA order with a scheduling barrier that every other instruction
 // class (VALU, SALU, LDS, VMEM, transcendental) may still cross.
 #define WATTN_PIN_MFMA() __builtin_amdgcn_sched_barrier(0x7F6)
+// The same, but LDS instructions stay in place too: used where the source
+// issues LDS reads a fixed distance ahead of the MFMAs that consume them.
+#define WATTN_PIN_MFMA_LDS() __builtin_amdgcn_sched_barrier(0x676)
 
 constexpr int kN = 144;
-constexpr int kNT = 9;           // key / query tiles of 16
-constexpr int kDH = 64;
-constexpr int kWaves = 3;
-constexpr int kQTPerWave = 3;
-constexpr int kThreads = kWaves * 64;
-constexpr int kKStride = 72;     // bf16 per K row in LDS
-constexpr int kVStride = 152;    // bf16 per V^T row in LDS
+constexpr int kNT = 9;            // key / query tiles of 16
+constexpr int kThreads = 256;     // 4 waves
+constexpr int kRowsPerThread = 5; // rows (tid >> 3) + 32 i, i < 5 (the 5th only for tid < 128)
+constexpr int kTensorBytes = kN * 128;
+constexpr int kKxOff = 3 * kTensorBytes;
+constexpr int kCodeOff = kKxOff + kN * 64;
+constexpr int kTokOff = kCodeOff + kN;
+constexpr int kSmemBytes = kTokOff + kN * 4;
 
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
+struct PParams {
+  int32_t X[3], P[3], shift[3], win[3], nwin[3];
+  int32_t special[3][3];
+  int32_t heads;
+  int32_t n_items;
+  float c2;
+  uint32_t beta01;  // bf16 beta term 0 | term 1 << 16
+  uint32_t beta2;   // bf16 beta term 2
+  uint32_t pad;     // bf16 padding-key offset
+  uint32_t slot[kN];
+};
 
-// d-row of V^T that A-operand row m of output tile t reads. Chosen so the
-// accumulator of tiles (0, 1) gives each lane dims [8g, 8g + 8) and tiles
-// (2, 3) dims [32 + 8g, 32 + 8g + 8): two contiguous 16-byte stores per lane.
-__device__ __forceinline__ int dmap(int t, int m) {
-  return (t >> 1) * 32 + (m >> 2) * 8 + (t & 1) * 4 + (m & 3);
-}
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
+// byte offset of 16-byte chunk c (0..7) of row r in a 128-byte-row tensor tile
+__device__ __forceinline__ int qkv_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+// byte offset of chunk c (0..3) of row r in the 64-byte-row mask-feature tile
+__device__ __forceinline__ int kx_off(int r, int c) { return kKxOff + r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// first dim of the 4-dim group q (0..3) held by output tile t (0..3); the
+// alternation of the +4 between neighbouring groups makes each transposed
+// read touch both 8-byte halves of the 16-byte chunks it spans
+__device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
 __device__ __forceinline__ float wave_max16x4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -247,197 +276,329 @@ __device__ __forceinline__ float wave_sum16x4(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void wattn_bf16_n144_d64(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ k,
-                                                               const uint16_t* __restrict__ v,
-                                                               uint16_t* __restrict__ o, Geom g) {
-  __shared__ __align__(16) uint16_t Ks[kN * kKStride];
-  __shared__ __align__(16) uint16_t Vt[kDH * kVStride];
-  __shared__ int32_t tokS[kN];
-  __shared__ __align__(16) uint8_t codeS[kN];
+struct WinPos {
+  int b, k[3];
+  bool masked;
+};
+
+// Window w (batch folded in) -> (b, kd, kh, kw) and whether it needs the
+// mask path (a region cut or padding along some axis).
+__device__ __forceinline__ WinPos decode_window(const PParams& p, int w) {
+  WinPos it;
+  const int per_b = p.nwin[0] * p.nwin[1] * p.nwin[2];
+  it.b = w / per_b;
+  w -= it.b * per_b;
+  it.k[0] = w / (p.nwin[1] * p.nwin[2]);
+  w -= it.k[0] * (p.nwin[1] * p.nwin[2]);
+  it.k[1] = w / p.nwin[2];
+  it.k[2] = w - it.k[1] * p.nwin[2];
+  bool m = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
+  it.masked = m;
+  return it;
+}
+
+// Grid position of slot (od, oh, ow) of a window: token index, or -1 for
+// padding, and the region code (one bit per axis: shifted axis and position
+// in the wrapped part [P - s, P)).
+__device__ __forceinline__ void map_slot(const PParams& p, const WinPos& it, uint32_t packed, int32_t& tok,
+                                         uint32_t& code) {
+  const int o[3] = {(int)(packed & 0xFF), (int)((packed >> 8) & 0xFF), (int)(packed >> 16)};
+  int g[3];
+  uint32_t c = 0;
+  bool valid = true;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int pa = it.k[a] * p.win[a] + o[a];
+    int ga = pa + p.shift[a];
+    ga = ga >= p.P[a] ? ga - p.P[a] : ga;
+    g[a] = ga;
+    valid = valid && ga < p.X[a];
+    c |= (p.shift[a] > 0 && pa >= p.P[a] - p.shift[a]) ? (1u << a) : 0u;
+  }
+  tok = valid ? ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2] : -1;
+  code = valid ? c : kPadCode;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
+
+__device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
+  typedef short4_t __attribute__((address_space(3))) * lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(smem + byte_off));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wattn_bf16_n144_d64(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const PParams p) {
+  __shared__ __align__(16) uint8_t smem[kSmemBytes];
+  uint8_t* codeS = smem + kCodeOff;
+  int32_t* tokS = reinterpret_cast<int32_t*>(smem + kTokOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
+  const int part = tid & 7;   // the 16-byte chunk of every row this thread moves
+  const int row0 = tid >> 3;  // its rows: row0 + 32 i
+  const int nrows = tid < 128 ? 5 : 4;
+  const int heads = p.heads;
+  const size_t RS = (size_t)heads * 64;
 
-  int b, kd, kh, kw, head;
-  decode_item(g, blockIdx.x, b, kd, kh, kw, head);
+  // contiguous item range of this workgroup; items are window-major, so the
+  // index map, region codes and mask features change once per `heads` items
+  const int64_t n_items = p.n_items;
+  int item = (int)((int64_t)blockIdx.x * n_items / gridDim.x);
+  const int end = (int)((int64_t)(blockIdx.x + 1) * n_items / gridDim.x);
+  if (item >= end) return;
 
-  int need_mask = 0;
-  if (tid < kN) {
-    int32_t t;
-    uint32_t c;
-    slot_map(g, b, kd, kh, kw, tid, t, c);
-    tokS[tid] = t;
-    codeS[tid] = (uint8_t)c;
-    need_mask = c != 0;
-  }
-  need_mask = __syncthreads_or(need_mask);
+  // this thread's rows of the window being prefetched: token index and code
+  int32_t ptok[kRowsPerThread];
+  uint32_t pcode[kRowsPerThread];
+  u32x4 pq[kRowsPerThread], pk[kRowsPerThread], pv[kRowsPerThread];
 
-  const size_t RS = (size_t)g.heads * kDH;
-  const size_t hoff = (size_t)head * kDH;
-
-  // ---- issue every global load of this (window, head) before any use ----
-  u32x4 kreg[6];
+  auto map_rows = [&](const WinPos& wp) {
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 3, part = c & 7;
-    const int32_t t = tokS[row];
-    kreg[i] = t >= 0 ? load16(k + (size_t)t * RS + hoff + part * 8) : u32x4{0, 0, 0, 0};
-  }
-  u32x4 va[3], vb[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int c = tid + kThreads * i;
-    const int pr = c >> 3, part = c & 7;
-    const int32_t t0 = tokS[2 * pr], t1 = tokS[2 * pr + 1];
-    va[i] = t0 >= 0 ? load16(v + (size_t)t0 * RS + hoff + part * 8) : u32x4{0, 0, 0, 0};
-    vb[i] = t1 >= 0 ? load16(v + (size_t)t1 * RS + hoff + part * 8) : u32x4{0, 0, 0, 0};
-  }
-  u32x4 qreg[kQTPerWave][2];
-#pragma unroll
-  for (int qi = 0; qi < kQTPerWave; ++qi) {
-    const int row = (wave * kQTPerWave + qi) * 16 + l16;
-    const int32_t t = tokS[row];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      qreg[qi][s] = t >= 0 ? load16(q + (size_t)t * RS + hoff + 32 * s + 8 * g4) : u32x4{0, 0, 0, 0};
-  }
-
-  // ---- K row-major into LDS; V transposed (pairs of keys per 32-bit write) ----
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 3, part = c & 7;
-    *reinterpret_cast<u32x4*>(&Ks[row * kKStride + part * 8]) = kreg[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int c = tid + kThreads * i;
-    const int pr = c >> 3, part = c & 7;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t a = va[i][j >> 1], bb = vb[i][j >> 1];
-      const uint32_t packed = (j & 1) ? ((a >> 16) | (bb & 0xFFFF0000u)) : ((a & 0xFFFFu) | (bb << 16));
-      *reinterpret_cast<uint32_t*>(&Vt[(part * 8 + j) * kVStride + 2 * pr]) = packed;
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      ptok[i] = -1;
+      pcode[i] = kPadCode;
+      if (i < nrows) map_slot(p, wp, p.slot[row0 + 32 * i], ptok[i], pcode[i]);
     }
-  }
-  __syncthreads();
+  };
+  auto issue_loads = [&](int head) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      pq[i] = pk[i] = pv[i] = u32x4{0, 0, 0, 0};
+      if (ptok[i] >= 0) {
+        const size_t off = (size_t)ptok[i] * RS + (size_t)head * 64 + part * 8;
+        pq[i] = ldg16(q + off);
+        pk[i] = ldg16(k + off);
+        pv[i] = ldg16(v + off);
+      }
+    }
+  };
 
-  const float c2 = g.c2;
+  int win = item / heads;
+  WinPos cur = decode_window(p, win);
+  map_rows(cur);
+  issue_loads(item - win * heads);
+  bool new_window = true;  // the item being staged starts a window in this workgroup
+
+  const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
+  const float c2 = p.c2;
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  int rot = blockIdx.x;
+
+  while (true) {
+    const int head = item - win * heads;
+    // ---- stage the item: registers -> LDS ----
 #pragma unroll
-  for (int qi = 0; qi < kQTPerWave; ++qi) {
-    const int qt = wave * kQTPerWave + qi;
-    // Consecutive MFMAs stay independent: the dims step is the outer loop.
-    floatx4 S[kNT];
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      if (i < nrows) {
+        const int r = row0 + 32 * i;
+        *reinterpret_cast<u32x4*>(smem + qkv_off(r, part)) = pq[i];
+        *reinterpret_cast<u32x4*>(smem + kTensorBytes + qkv_off(r, part)) = pk[i];
+        *reinterpret_cast<u32x4*>(smem + 2 * kTensorBytes + qkv_off(r, part)) = pv[i];
+        if (new_window) {
+          if (part == 0) {
+            codeS[r] = (uint8_t)pcode[i];
+            tokS[r] = ptok[i];
+          }
+          if (cur.masked && part < 4) {
+            // mask features of key r, 8 dims per chunk: chunks 0..2 hold a
+            // bias term at every region other than the key's own, chunk 3
+            // the padding offset
+            const uint32_t ck = pcode[i];
+            u32x4 w = u32x4{0, 0, 0, 0};
+            if (ck == kPadCode) {
+              if (part == 3) w[0] = p.pad;
+            } else if (part < 3) {
+              const uint32_t bt = beta[part];
 #pragma unroll
-    for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int kt = 0; kt < kNT; ++kt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[(kt * 16 + l16) * kKStride + 32 * s + 8 * g4]);
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, qreg[qi][s]), S[kt], 0, 0, 0);
-        WATTN_PIN_MFMA();
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = (uint32_t)(2 * e) != ck ? bt : 0u;
+                const uint32_t hi = (uint32_t)(2 * e + 1) != ck ? bt : 0u;
+                w[e] = lo | (hi << 16);
+              }
+            }
+            *reinterpret_cast<u32x4*>(smem + kx_off(r, part)) = w;
+          }
+        }
       }
     }
 
-    float mx = -INFINITY;
-    if (!need_mask) {
+    // ---- prefetch the next item while this one is computed (its registers
+    // were just staged, so the loads can go out before the barrier) ----
+    const int next = item + 1;
+    const bool has_next = next < end;
+    int next_win = win;
+    WinPos nxt = cur;
+    if (has_next) {
+      next_win = next / heads;
+      if (next_win != win) {
+        nxt = decode_window(p, next_win);
+        map_rows(nxt);
+      }
+      issue_loads(next - next_win * heads);
+    }
+    __syncthreads();
+
+    // ---- compute: 9 query tiles over 4 waves; the wave with 3 tiles rotates ----
+    const size_t hoff = (size_t)head * 64;
+    for (int qt = (wave - rot) & 3; qt < kNT; qt += 4) {
+      bf16x8_t qop[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        qop[s] = *reinterpret_cast<const bf16x8_t*>(smem + qkv_off(qt * 16 + l16, 4 * s + g4));
+
+      floatx4 S[kNT];
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // Consecutive MFMAs are independent (the dims step is the outer loop);
+      // the K fragments are read kAhead MFMAs before use so LDS latency hides.
+      {
+        constexpr int kAhead = 8;
+        bf16x8_t kf[2 * kNT];
+        auto kread = [&](int idx) {
+          const int s = idx / kNT, kt = idx % kNT;
+          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + kTensorBytes + qkv_off(kt * 16 + l16, 4 * s + g4));
+        };
+#pragma unroll
+        for (int idx = 0; idx < kAhead; ++idx) kread(idx);
+#pragma unroll
+        for (int idx = 0; idx < 2 * kNT; ++idx) {
+          const int s = idx / kNT, kt = idx % kNT;
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], qop[s], S[kt], 0, 0, 0);
+          WATTN_PIN_MFMA_LDS();
+          if (idx + kAhead < 2 * kNT) kread(idx + kAhead);
+        }
+      }
+      if (cur.masked) {
+        const uint32_t cq = codeS[qt * 16 + l16];
+        u32x4 qx = u32x4{0, 0, 0, 0};
+        if (g4 < 3) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            qx[e] = (cq == (uint32_t)(2 * e) ? 0x3F80u : 0u) | (cq == (uint32_t)(2 * e + 1) ? 0x3F800000u : 0u);
+        } else {
+          qx[0] = 0x3F80u;  // 1.0 in the pad column
+        }
+        const bf16x8_t qxb = __builtin_bit_cast(bf16x8_t, qx);
+        bf16x8_t xf[kNT];
+#pragma unroll
+        for (int kt = 0; kt < kNT; ++kt)
+          xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kx_off(kt * 16 + l16, g4));
+#pragma unroll
+        for (int kt = 0; kt < kNT; ++kt) {
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
+          WATTN_PIN_MFMA_LDS();
+        }
+      }
+
+      // ---- FP32 softmax numerators over the 144 keys of each query (log2 domain) ----
+      float mx = S[0][0];
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
       mx = wave_max16x4(mx);
       const float nm = -mx * c2;
+      bf16x8_t Pb[4];
+      bf16x4_t Pt;
 #pragma unroll
-      for (int kt = 0; kt < kNT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
-    } else {
-      const uint32_t cq = codeS[qt * 16 + l16];
-      const float bias2 = g.bias2;
-#pragma unroll
-      for (int kt = 0; kt < kNT; ++kt) {
-        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(&codeS[kt * 16 + 4 * g4]);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t ck = (c4 >> (8 * i)) & 0xFFu;
-          float add = ck == cq ? 0.f : bias2;
-          add = ck == kPadCode ? -INFINITY : add;
-          const float x = fmaf(S[kt][i], c2, add);
-          S[kt][i] = x;
-          mx = fmaxf(mx, x);
+          Pb[j][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j][i], c2, nm));
+          Pb[j][4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j + 1][i], c2, nm));
         }
-      }
-      mx = wave_max16x4(mx);
 #pragma unroll
-      for (int kt = 0; kt < kNT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[kt][i] = __builtin_amdgcn_exp2f(S[kt][i] - mx);
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < kNT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum += S[kt][i];
-    sum = wave_sum16x4(sum);
-    const float inv = 1.0f / sum;
+      for (int i = 0; i < 4; ++i) Pt[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[8][i], c2, nm));
 
-    bf16x8_t Pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Pb[j][i] = (__bf16)S[2 * j][i];
-        Pb[j][4 + i] = (__bf16)S[2 * j + 1][i];
-      }
-    }
-    bf16x4_t Pt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Pt[i] = (__bf16)S[8][i];
-
-    // Four independent accumulators, key step outer; the 16-key tail goes
-    // first so it never waits on a fresh accumulator.
-    floatx4 O[4];
-    const uint16_t* vrow[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      vrow[t] = &Vt[dmap(t, l16) * kVStride];
-      const short4_t a4 = *reinterpret_cast<const short4_t*>(vrow[t] + 128 + 4 * g4);
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, __builtin_bit_cast(short4_t, Pt),
-                                                       floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      WATTN_PIN_MFMA();
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      // ---- O^T = V^T P^T and the row sums (an all-ones A operand) ----
+      // tail keys first, then four key steps of 32; as an input lane of the
+      // transposed read this lane points at key (base + e), dims dbase(t, qd)..+3
+      const int e = l16 >> 2, qd = l16 & 3;
+      auto v_off = [&](int key, int d) { return 2 * kTensorBytes + qkv_off(key, d >> 3) + ((d & 4) << 1); };
+      floatx4 O[4], L;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow[t] + 32 * j + 4 * g4);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow[t] + 32 * j + 16 + 4 * g4);
-        const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), Pb[j], O[t], 0, 0, 0);
+        const short4_t a4 = lds_tr(smem, v_off(128 + 4 * g4 + e, dbase(t, qd)));
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, __builtin_bit_cast(short4_t, Pt),
+                                                         floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         WATTN_PIN_MFMA();
       }
-    }
-
-    const int32_t t = tokS[qt * 16 + l16];
-    if (t >= 0) {
-      uint16_t* out = o + (size_t)t * RS + hoff;
-      bf16x8_t r0, r1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r0[i] = (__bf16)(O[0][i] * inv);
-        r0[4 + i] = (__bf16)(O[1][i] * inv);
-        r1[i] = (__bf16)(O[2][i] * inv);
-        r1[4 + i] = (__bf16)(O[3][i] * inv);
+      {
+        const u32x2 ones2 = u32x2{0x3F803F80u, 0x3F803F80u};
+        L = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones2),
+                                                      __builtin_bit_cast(short4_t, Pt),
+                                                      floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        WATTN_PIN_MFMA();
       }
-      *reinterpret_cast<bf16x8_t*>(out + 8 * g4) = r0;
-      *reinterpret_cast<bf16x8_t*>(out + 32 + 8 * g4) = r1;
+      // V^T fragments of key step j + 1 are read while step j runs
+      u32x4 vf[2][4];
+      auto vread = [&](int j, int buf) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const short4_t lo = lds_tr(smem, v_off(32 * j + 4 * g4 + e, dbase(t, qd)));
+          const short4_t hi = lds_tr(smem, v_off(32 * j + 16 + 4 * g4 + e, dbase(t, qd)));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          vf[buf][t] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        }
+      };
+      vread(0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j + 1 < 4) vread(j + 1, (j + 1) & 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
+          WATTN_PIN_MFMA_LDS();
+        }
+        L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[j], L, 0, 0, 0);
+        WATTN_PIN_MFMA_LDS();
+      }
+
+      // ---- scatter O rows straight to grid layout (padding rows are cropped) ----
+      // The tile goes through its own Q rows in LDS (no longer needed) so that
+      // each store instruction writes eight whole 128-byte rows.
+      {
+        const float inv = __builtin_amdgcn_rcpf(L[0]);
+        const int r = qt * 16 + l16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int d = dbase(t, g4);
+          const u32x2 w = u32x2{pack_bf16x2(O[t][0] * inv, O[t][1] * inv), pack_bf16x2(O[t][2] * inv, O[t][3] * inv)};
+          *reinterpret_cast<u32x2*>(smem + qkv_off(r, d >> 3) + ((d & 4) << 1)) = w;
+        }
+        const int rr = lane >> 3, cc = lane & 7;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = qt * 16 + 8 * h + rr;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(smem + qkv_off(row, cc));
+          const int32_t tq = tokS[row];
+          if (tq >= 0) *reinterpret_cast<u32x4*>(o + (size_t)tq * RS + hoff + cc * 8) = w;
+        }
+      }
     }
+    __syncthreads();  // LDS is free for the next item
+    if (!has_next) break;
+    new_window = next_win != win;
+    item = next;
+    win = next_win;
+    cur = nxt;
+    ++rot;
   }
 }
 
@@ -485,6 +646,53 @@ hipError_t launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, 
                          dim3(p->threads), args, f32_lds_bytes(p->N, DH), s);
 }
 
+// Workgroups resident per CU for the bf16 kernel (LDS and registers allow two).
+constexpr int kBf16WgPerCu = 2;
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+                       hipStream_t s) {
+  PParams p;
+  const swin3d_wattn_desc_t& d = pl->desc;
+  p.X[0] = d.D;
+  p.X[1] = d.H;
+  p.X[2] = d.W;
+  for (int a = 0; a < 3; ++a) {
+    p.P[a] = pl->padded[a];
+    p.shift[a] = d.shift[a];
+    p.win[a] = d.window[a];
+    p.nwin[a] = pl->nwin[a];
+    for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
+  }
+  p.heads = d.heads;
+  p.n_items = (int32_t)pl->n_items;
+  p.c2 = pl->c2;
+  p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
+  p.beta2 = pl->beta_bf16[2];
+  p.pad = pl->pad_bf16;
+  for (int n = 0; n < kN; ++n) p.slot[n] = pl->slot[n];
+  int64_t grid = (int64_t)cu_count() * kBf16WgPerCu;
+  if (grid > pl->n_items) grid = pl->n_items;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  void* args[] = {&qq, &kk, &vv, &oo, &p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_n144_d64), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, s);
+}
+
 }  // namespace
 
 int swin3d_wattn_launch(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
@@ -492,14 +700,7 @@ int swin3d_wattn_launch(const swin3d_wattn_plan* p, const void* q, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->kernel == 1) {
-    Geom g = make_geom(p);
-    const uint16_t* qq = static_cast<const uint16_t*>(q);
-    const uint16_t* kk = static_cast<const uint16_t*>(k);
-    const uint16_t* vv = static_cast<const uint16_t*>(v);
-    uint16_t* oo = static_cast<uint16_t*>(o);
-    void* args[] = {&qq, &kk, &vv, &oo, &g};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_n144_d64), dim3((unsigned)p->workgroups),
-                        dim3(kThreads), args, 0, s);
+    e = launch_bf16(p, q, k, v, o, s);
   } else if (p->desc.head_dim == 32) {
     e = launch_f32<32>(p, q, k, v, o, s);
   } else {

@@ -15,10 +15,20 @@ struct swin3d_wattn_plan {
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
   int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA
-  int64_t workgroups;
+  int64_t workgroups;       // for kernel 1: an upper bound, the launch uses min(items, 2 per CU)
   int32_t threads;
+  int64_t n_items;          // n_windows * heads
   float c2;                 // scale * log2(e)
   float bias2;              // cross_region_bias * log2(e)
+  // bf16 kernel: the cross-region bias divided by scale, split into three
+  // bf16 terms whose sum is exact to float precision, and the padding-key
+  // offset (-2^100: its exponential underflows to exactly zero)
+  uint16_t beta_bf16[3];
+  uint16_t pad_bf16;
+  // per axis: window indices that hold a region cut or padding (-1 = none)
+  int32_t special[3][3];
+  // slot n of a window -> (od, oh, ow) packed as od | oh << 8 | ow << 16
+  uint32_t slot[256];
 };
 
 // Defined in kernels.hip. Launches the plan's kernel; returns a swin3d code.
