@@ -122,6 +122,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-ms", type=float, default=300.0, help="minimum warm-up time on the GPU")
     ap.add_argument("--bias", type=float, default=-100.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,10 +156,20 @@ def main():
     info = plan.info()
     stream = torch.cuda.current_stream(dev)
 
+    # warm-up: the requested steps, then more until the GPU has run the kernel for
+    # --warmup-ms (engine clocks ramp up under sustained load; a cold first pass
+    # reads about 10% slow)
     for _ in range(args.warmup):
         plan.run(x["q"], x["k"], x["v"], o)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    extra = 0
+    while (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
+        for _ in range(20):
+            plan.run(x["q"], x["k"], x["v"], o)
+        torch.cuda.synchronize()
+        extra += 20
+    log(f"[bench] warmup {args.warmup} + {extra} steps done; timing {args.steps} steps")
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -602,6 +602,247 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+// ---------------------------------------------------------------------------
+// Non-persistent variant: one workgroup per (window, head) item, dispatched
+// head-major (item = head * n_windows + window), WAVES5 waves. K, V, mask
+// features and the slot table live in LDS; each wave loads the Q operands of
+// its own query tiles straight into registers.
+// ---------------------------------------------------------------------------
+#ifndef WAVES5
+#define WAVES5 4
+#endif
+#ifndef ORDER5
+#define ORDER5 0
+#endif
+constexpr int kThreads5 = 64 * WAVES5;
+// mask-feature table: the A fragment (8 bf16) of a key depends only on its
+// region code (0..7, or 8 for padding) and on the lane's 8-dim group (0..3)
+constexpr int kXt5 = 2 * kTensorBytes;
+constexpr int kCode5 = kXt5 + 9 * 4 * 16;
+constexpr int kTok5 = kCode5 + kN;
+constexpr int kSmem5 = kTok5 + kN * 4;
+
+__global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) void wattn_bf16_item(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const PParams p) {
+  __shared__ __align__(16) uint8_t smem[kSmem5];
+  uint8_t* codeS = smem + kCode5;
+  int32_t* tokS = reinterpret_cast<int32_t*>(smem + kTok5);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const int heads = p.heads;
+  const size_t RS = (size_t)heads * 64;
+  const int n_windows = p.n_items / heads;
+  const int item = blockIdx.x;
+#if ORDER5 == 1
+  const int win = item / heads;
+  const int head = item - win * heads;
+#else
+  const int head = item / n_windows;
+  const int win = item - head * n_windows;
+#endif
+  const WinPos cur = decode_window(p, win);
+  const size_t hoff = (size_t)head * 64;
+
+  // ---- slot table of the window ----
+  uint32_t mycode = kPadCode;
+  for (int r = tid; r < kN; r += kThreads5) {
+    int32_t t;
+    map_slot(p, cur, p.slot[r], t, mycode);
+    tokS[r] = t;
+    codeS[r] = (uint8_t)mycode;
+  }
+  __syncthreads();
+
+  // ---- gather: K and V rows into registers, Q operands of this wave's tiles ----
+  constexpr int kChunks = kN * 8;
+  constexpr int kPer = (kChunks + kThreads5 - 1) / kThreads5;
+  u32x4 kr[kPer], vr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int c = tid + kThreads5 * j;
+    kr[j] = vr[j] = u32x4{0, 0, 0, 0};
+    if (c < kChunks) {
+      const int32_t t = tokS[c >> 3];
+      if (t >= 0) {
+        const size_t off = (size_t)t * RS + hoff + (c & 7) * 8;
+        kr[j] = ldg16(k + off);
+        vr[j] = ldg16(v + off);
+      }
+    }
+  }
+  constexpr int kMaxQT = (kNT + WAVES5 - 1) / WAVES5;
+  u32x4 qr[kMaxQT][2];
+#pragma unroll
+  for (int qi = 0; qi < kMaxQT; ++qi) {
+    const int qt = wave + WAVES5 * qi;
+    qr[qi][0] = qr[qi][1] = u32x4{0, 0, 0, 0};
+    if (qt < kNT) {
+      const int32_t t = tokS[qt * 16 + l16];
+      if (t >= 0) {
+        const size_t off = (size_t)t * RS + hoff + 8 * g4;
+        qr[qi][0] = ldg16(q + off);
+        qr[qi][1] = ldg16(q + off + 32);
+      }
+    }
+  }
+  // mask-feature table (only windows with a cut or padding use it)
+  if (cur.masked && tid < 36) {
+    const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
+    const uint32_t ck = tid >> 2, part = tid & 3;  // ck == 8: padding key
+    u32x4 w = u32x4{0, 0, 0, 0};
+    if (ck == 8) {
+      if (part == 3) w[0] = p.pad;
+    } else if (part < 3) {
+      const uint32_t bt = beta[part];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (uint32_t)(2 * e) != ck ? bt : 0u;
+        const uint32_t hi = (uint32_t)(2 * e + 1) != ck ? bt : 0u;
+        w[e] = lo | (hi << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(smem + kXt5 + tid * 16) = w;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int c = tid + kThreads5 * j;
+    if (c < kChunks) {
+      *reinterpret_cast<u32x4*>(smem + qkv_off(c >> 3, c & 7)) = kr[j];
+      *reinterpret_cast<u32x4*>(smem + kTensorBytes + qkv_off(c >> 3, c & 7)) = vr[j];
+    }
+  }
+  __syncthreads();
+
+  const float c2 = p.c2;
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+  for (int qi = 0; qi < kMaxQT; ++qi) {
+    const int qt = wave + WAVES5 * qi;
+    if (qt >= kNT) break;
+    const bf16x8_t qop[2] = {__builtin_bit_cast(bf16x8_t, qr[qi][0]), __builtin_bit_cast(bf16x8_t, qr[qi][1])};
+
+    floatx4 S[kNT];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int kAhead = 8;
+      bf16x8_t kf[2 * kNT];
+      auto kread = [&](int idx) {
+        const int s = idx / kNT, kt = idx % kNT;
+        kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + qkv_off(kt * 16 + l16, 4 * s + g4));
+      };
+#pragma unroll
+      for (int idx = 0; idx < kAhead; ++idx) kread(idx);
+#pragma unroll
+      for (int idx = 0; idx < 2 * kNT; ++idx) {
+        const int s = idx / kNT, kt = idx % kNT;
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], qop[s], S[kt], 0, 0, 0);
+        WATTN_PIN_MFMA_LDS();
+        if (idx + kAhead < 2 * kNT) kread(idx + kAhead);
+      }
+    }
+    if (cur.masked) {
+      const uint32_t cq = codeS[qt * 16 + l16];
+      u32x4 qx = u32x4{0, 0, 0, 0};
+      if (g4 < 3) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qx[e] = (cq == (uint32_t)(2 * e) ? 0x3F80u : 0u) | (cq == (uint32_t)(2 * e + 1) ? 0x3F800000u : 0u);
+      } else {
+        qx[0] = 0x3F80u;
+      }
+      const bf16x8_t qxb = __builtin_bit_cast(bf16x8_t, qx);
+      bf16x8_t xf[kNT];
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) {
+        const uint32_t ck = codeS[kt * 16 + l16];
+        const uint32_t row = ck == kPadCode ? 8u : ck;
+        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kXt5 + (row * 4 + g4) * 16);
+      }
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) {
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
+        WATTN_PIN_MFMA_LDS();
+      }
+    }
+
+    float mx = S[0][0];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
+    mx = wave_max16x4(mx);
+    const float nm = -mx * c2;
+    bf16x8_t Pb[4];
+    bf16x4_t Pt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Pb[j][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j][i], c2, nm));
+        Pb[j][4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j + 1][i], c2, nm));
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Pt[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[8][i], c2, nm));
+
+    const int e = l16 >> 2, qd = l16 & 3;
+    auto v_off = [&](int key, int d) { return kTensorBytes + qkv_off(key, d >> 3) + ((d & 4) << 1); };
+    floatx4 O[4], L;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const short4_t a4 = lds_tr(smem, v_off(128 + 4 * g4 + e, dbase(t, qd)));
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, __builtin_bit_cast(short4_t, Pt),
+                                                       floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      WATTN_PIN_MFMA();
+    }
+    {
+      const u32x2 ones2 = u32x2{0x3F803F80u, 0x3F803F80u};
+      L = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones2),
+                                                    __builtin_bit_cast(short4_t, Pt), floatx4{0.f, 0.f, 0.f, 0.f},
+                                                    0, 0, 0);
+      WATTN_PIN_MFMA();
+    }
+    u32x4 vf[2][4];
+    auto vread = [&](int j, int buf) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const short4_t lo = lds_tr(smem, v_off(32 * j + 4 * g4 + e, dbase(t, qd)));
+        const short4_t hi = lds_tr(smem, v_off(32 * j + 16 + 4 * g4 + e, dbase(t, qd)));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        vf[buf][t] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+    };
+    vread(0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j + 1 < 4) vread(j + 1, (j + 1) & 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
+        WATTN_PIN_MFMA_LDS();
+      }
+      L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[j], L, 0, 0, 0);
+      WATTN_PIN_MFMA_LDS();
+    }
+
+    const int32_t tq = tokS[qt * 16 + l16];
+    if (tq >= 0) {
+      const float inv = __builtin_amdgcn_rcpf(L[0]);
+      uint16_t* out = o + (size_t)tq * RS + hoff;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x2 w = u32x2{pack_bf16x2(O[t][0] * inv, O[t][1] * inv), pack_bf16x2(O[t][2] * inv, O[t][3] * inv)};
+        *reinterpret_cast<u32x2*>(out + dbase(t, g4)) = w;
+      }
+    }
+  }
+}
+
 Geom make_geom(const swin3d_wattn_plan* p) {
   Geom g;
   const swin3d_wattn_desc_t& d = p->desc;
@@ -682,15 +923,20 @@ hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k
   p.beta2 = pl->beta_bf16[2];
   p.pad = pl->pad_bf16;
   for (int n = 0; n < kN; ++n) p.slot[n] = pl->slot[n];
-  int64_t grid = (int64_t)cu_count() * kBf16WgPerCu;
-  if (grid > pl->n_items) grid = pl->n_items;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
+#ifdef WATTN_PERSISTENT
+  int64_t grid = (int64_t)cu_count() * kBf16WgPerCu;
+  if (grid > pl->n_items) grid = pl->n_items;
   return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_n144_d64), dim3((unsigned)grid),
                          dim3(kThreads), args, 0, s);
+#else
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_item), dim3((unsigned)pl->n_items),
+                         dim3(kThreads5), args, 0, s);
+#endif
 }
 
 }  // namespace
