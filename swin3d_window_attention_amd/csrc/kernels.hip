@@ -184,21 +184,19 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// BF16 path: persistent matrix-core kernel for N = 144 tokens per window
-// (window (2, 6, 12) or any other with 144 slots), head_dim 64.
+// BF16 path: matrix-core kernel for N = 144 tokens per window (window
+// (2, 6, 12) or any other with 144 slots) and head_dim 64.
 //
-// Work: items are (window, head) pairs, item = window * heads + head; each
-// workgroup owns a contiguous range of items, so the index map, the region
-// codes and the mask features are rebuilt only when its window changes.
-// While it computes one item, each thread already holds the next item's
-// Q, K, V rows in registers (global loads in flight), so HBM latency hides
-// behind the matrix and softmax work.
+// Work: one workgroup of four waves per (window, head) item, dispatched
+// head-major (item = head * n_windows + window): the workgroups in flight
+// read one head of many neighbouring windows, the order HBM serves best for
+// these 128-byte rows. Small workgroups (38 KB of LDS, <= 128 VGPRs) let four
+// of them share a CU, so one workgroup's loads overlap another's math.
 //
-// LDS per item: Q, K, V row-major (128 B rows, 16-byte chunks XOR-swizzled
-// by row bits 1..3 so the operand reads below hit 16 distinct bank groups);
-// per window: the mask features of K, the region code and token of each slot.
-// Row sums of P come from the matrix core too: a fifth accumulator whose A
-// operand is all ones, so the normaliser sums the same bf16 P as the output.
+// LDS: K and V row-major (128 B rows, 16-byte chunks XOR-swizzled by row
+// bits 1..3 so that every operand read below hits distinct bank groups),
+// the slot table (token index, region code) and a small mask-feature table.
+// Each wave loads the Q operands of its own query tiles into registers.
 //
 // S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims, B = 32
 // dims x 16 queries). Its accumulator gives each lane four keys of one
@@ -209,10 +207,13 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
 //
 // Mask on the matrix core: a third k-step of 32 extra "dims" adds the
 // shifted-window bias. Q gets a one-hot of its region in each of three
-// 8-wide slots (plus a constant 1 in a pad column); K gets bias/scale
-// (split into three bf16 terms) at every region other than its own, and
-// -2^100 in the pad column when it is padding. The product adds exactly the
-// bias where regions differ and pushes padding keys to a zero weight.
+// 8-wide slots (plus a constant 1 in a pad column); K gets bias/scale (split
+// into three bf16 terms) at every region other than its own, and -2^100 in
+// the pad column when it is padding. The product adds exactly the bias
+// where regions differ and pushes padding keys to a zero weight. A key's
+// features depend only on its region code, so they come from a table.
+// Row sums of P come from the matrix core too: a fifth accumulator whose A
+// operand is all ones, so the normaliser sums the same bf16 P as the output.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short short4_t __attribute__((__vector_size__(8)));
@@ -233,16 +234,19 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 #define WATTN_PIN_MFMA_LDS() __builtin_amdgcn_sched_barrier(0x676)
 
 constexpr int kN = 144;
-constexpr int kNT = 9;            // key / query tiles of 16
-constexpr int kThreads = 256;     // 4 waves
-constexpr int kRowsPerThread = 5; // rows (tid >> 3) + 32 i, i < 5 (the 5th only for tid < 128)
-constexpr int kTensorBytes = kN * 128;
-constexpr int kKxOff = 3 * kTensorBytes;
-constexpr int kCodeOff = kKxOff + kN * 64;
+constexpr int kNT = 9;                    // key / query tiles of 16
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxQT = (kNT + kWaves - 1) / kWaves;  // query tiles per wave (at most)
+constexpr int kTensorBytes = kN * 128;    // one 144 x 64 bf16 tile
+// LDS layout (bytes): K tile, V tile, mask-feature table (9 codes x 4
+// groups x 16 B; code 8 = padding), region code and token of each slot
+constexpr int kXtOff = 2 * kTensorBytes;
+constexpr int kCodeOff = kXtOff + 9 * 4 * 16;
 constexpr int kTokOff = kCodeOff + kN;
 constexpr int kSmemBytes = kTokOff + kN * 4;
 
-struct PParams {
+struct AttnParams {
   int32_t X[3], P[3], shift[3], win[3], nwin[3];
   int32_t special[3][3];
   int32_t heads;
@@ -257,8 +261,6 @@ struct PParams {
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
 // byte offset of 16-byte chunk c (0..7) of row r in a 128-byte-row tensor tile
 __device__ __forceinline__ int qkv_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
-// byte offset of chunk c (0..3) of row r in the 64-byte-row mask-feature tile
-__device__ __forceinline__ int kx_off(int r, int c) { return kKxOff + r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 // first dim of the 4-dim group q (0..3) held by output tile t (0..3); the
 // alternation of the +4 between neighbouring groups makes each transposed
 // read touch both 8-byte halves of the 16-byte chunks it spans
@@ -270,12 +272,6 @@ __device__ __forceinline__ float wave_max16x4(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_sum16x4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
 struct WinPos {
   int b, k[3];
   bool masked;
@@ -283,7 +279,7 @@ struct WinPos {
 
 // Window w (batch folded in) -> (b, kd, kh, kw) and whether it needs the
 // mask path (a region cut or padding along some axis).
-__device__ __forceinline__ WinPos decode_window(const PParams& p, int w) {
+__device__ __forceinline__ WinPos decode_window(const AttnParams& p, int w) {
   WinPos it;
   const int per_b = p.nwin[0] * p.nwin[1] * p.nwin[2];
   it.b = w / per_b;
@@ -304,7 +300,7 @@ __device__ __forceinline__ WinPos decode_window(const PParams& p, int w) {
 // Grid position of slot (od, oh, ow) of a window: token index, or -1 for
 // padding, and the region code (one bit per axis: shifted axis and position
 // in the wrapped part [P - s, P)).
-__device__ __forceinline__ void map_slot(const PParams& p, const WinPos& it, uint32_t packed, int32_t& tok,
+__device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, uint32_t packed, int32_t& tok,
                                          uint32_t& code) {
   const int o[3] = {(int)(packed & 0xFF), (int)((packed >> 8) & 0xFF), (int)(packed >> 16)};
   int g[3];
@@ -338,296 +334,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wattn_bf16_n144_d64(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void wattn_bf16_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, const PParams p) {
+    uint16_t* __restrict__ o, const AttnParams p) {
   __shared__ __align__(16) uint8_t smem[kSmemBytes];
   uint8_t* codeS = smem + kCodeOff;
   int32_t* tokS = reinterpret_cast<int32_t*>(smem + kTokOff);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
-  const int part = tid & 7;   // the 16-byte chunk of every row this thread moves
-  const int row0 = tid >> 3;  // its rows: row0 + 32 i
-  const int nrows = tid < 128 ? 5 : 4;
-  const int heads = p.heads;
-  const size_t RS = (size_t)heads * 64;
-
-  // contiguous item range of this workgroup; items are window-major, so the
-  // index map, region codes and mask features change once per `heads` items
-  const int64_t n_items = p.n_items;
-  int item = (int)((int64_t)blockIdx.x * n_items / gridDim.x);
-  const int end = (int)((int64_t)(blockIdx.x + 1) * n_items / gridDim.x);
-  if (item >= end) return;
-
-  // this thread's rows of the window being prefetched: token index and code
-  int32_t ptok[kRowsPerThread];
-  uint32_t pcode[kRowsPerThread];
-  u32x4 pq[kRowsPerThread], pk[kRowsPerThread], pv[kRowsPerThread];
-
-  auto map_rows = [&](const WinPos& wp) {
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      ptok[i] = -1;
-      pcode[i] = kPadCode;
-      if (i < nrows) map_slot(p, wp, p.slot[row0 + 32 * i], ptok[i], pcode[i]);
-    }
-  };
-  auto issue_loads = [&](int head) {
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      pq[i] = pk[i] = pv[i] = u32x4{0, 0, 0, 0};
-      if (ptok[i] >= 0) {
-        const size_t off = (size_t)ptok[i] * RS + (size_t)head * 64 + part * 8;
-        pq[i] = ldg16(q + off);
-        pk[i] = ldg16(k + off);
-        pv[i] = ldg16(v + off);
-      }
-    }
-  };
-
-  int win = item / heads;
-  WinPos cur = decode_window(p, win);
-  map_rows(cur);
-  issue_loads(item - win * heads);
-  bool new_window = true;  // the item being staged starts a window in this workgroup
-
-  const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
-  const float c2 = p.c2;
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
-  int rot = blockIdx.x;
-
-  while (true) {
-    const int head = item - win * heads;
-    // ---- stage the item: registers -> LDS ----
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      if (i < nrows) {
-        const int r = row0 + 32 * i;
-        *reinterpret_cast<u32x4*>(smem + qkv_off(r, part)) = pq[i];
-        *reinterpret_cast<u32x4*>(smem + kTensorBytes + qkv_off(r, part)) = pk[i];
-        *reinterpret_cast<u32x4*>(smem + 2 * kTensorBytes + qkv_off(r, part)) = pv[i];
-        if (new_window) {
-          if (part == 0) {
-            codeS[r] = (uint8_t)pcode[i];
-            tokS[r] = ptok[i];
-          }
-          if (cur.masked && part < 4) {
-            // mask features of key r, 8 dims per chunk: chunks 0..2 hold a
-            // bias term at every region other than the key's own, chunk 3
-            // the padding offset
-            const uint32_t ck = pcode[i];
-            u32x4 w = u32x4{0, 0, 0, 0};
-            if (ck == kPadCode) {
-              if (part == 3) w[0] = p.pad;
-            } else if (part < 3) {
-              const uint32_t bt = beta[part];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = (uint32_t)(2 * e) != ck ? bt : 0u;
-                const uint32_t hi = (uint32_t)(2 * e + 1) != ck ? bt : 0u;
-                w[e] = lo | (hi << 16);
-              }
-            }
-            *reinterpret_cast<u32x4*>(smem + kx_off(r, part)) = w;
-          }
-        }
-      }
-    }
-
-    // ---- prefetch the next item while this one is computed (its registers
-    // were just staged, so the loads can go out before the barrier) ----
-    const int next = item + 1;
-    const bool has_next = next < end;
-    int next_win = win;
-    WinPos nxt = cur;
-    if (has_next) {
-      next_win = next / heads;
-      if (next_win != win) {
-        nxt = decode_window(p, next_win);
-        map_rows(nxt);
-      }
-      issue_loads(next - next_win * heads);
-    }
-    __syncthreads();
-
-    // ---- compute: 9 query tiles over 4 waves; the wave with 3 tiles rotates ----
-    const size_t hoff = (size_t)head * 64;
-    for (int qt = (wave - rot) & 3; qt < kNT; qt += 4) {
-      bf16x8_t qop[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        qop[s] = *reinterpret_cast<const bf16x8_t*>(smem + qkv_off(qt * 16 + l16, 4 * s + g4));
-
-      floatx4 S[kNT];
-#pragma unroll
-      for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      // Consecutive MFMAs are independent (the dims step is the outer loop);
-      // the K fragments are read kAhead MFMAs before use so LDS latency hides.
-      {
-        constexpr int kAhead = 8;
-        bf16x8_t kf[2 * kNT];
-        auto kread = [&](int idx) {
-          const int s = idx / kNT, kt = idx % kNT;
-          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + kTensorBytes + qkv_off(kt * 16 + l16, 4 * s + g4));
-        };
-#pragma unroll
-        for (int idx = 0; idx < kAhead; ++idx) kread(idx);
-#pragma unroll
-        for (int idx = 0; idx < 2 * kNT; ++idx) {
-          const int s = idx / kNT, kt = idx % kNT;
-          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], qop[s], S[kt], 0, 0, 0);
-          WATTN_PIN_MFMA_LDS();
-          if (idx + kAhead < 2 * kNT) kread(idx + kAhead);
-        }
-      }
-      if (cur.masked) {
-        const uint32_t cq = codeS[qt * 16 + l16];
-        u32x4 qx = u32x4{0, 0, 0, 0};
-        if (g4 < 3) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            qx[e] = (cq == (uint32_t)(2 * e) ? 0x3F80u : 0u) | (cq == (uint32_t)(2 * e + 1) ? 0x3F800000u : 0u);
-        } else {
-          qx[0] = 0x3F80u;  // 1.0 in the pad column
-        }
-        const bf16x8_t qxb = __builtin_bit_cast(bf16x8_t, qx);
-        bf16x8_t xf[kNT];
-#pragma unroll
-        for (int kt = 0; kt < kNT; ++kt)
-          xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kx_off(kt * 16 + l16, g4));
-#pragma unroll
-        for (int kt = 0; kt < kNT; ++kt) {
-          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
-          WATTN_PIN_MFMA_LDS();
-        }
-      }
-
-      // ---- FP32 softmax numerators over the 144 keys of each query (log2 domain) ----
-      float mx = S[0][0];
-#pragma unroll
-      for (int kt = 0; kt < kNT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
-      mx = wave_max16x4(mx);
-      const float nm = -mx * c2;
-      bf16x8_t Pb[4];
-      bf16x4_t Pt;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Pb[j][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j][i], c2, nm));
-          Pb[j][4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * j + 1][i], c2, nm));
-        }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Pt[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[8][i], c2, nm));
-
-      // ---- O^T = V^T P^T and the row sums (an all-ones A operand) ----
-      // tail keys first, then four key steps of 32; as an input lane of the
-      // transposed read this lane points at key (base + e), dims dbase(t, qd)..+3
-      const int e = l16 >> 2, qd = l16 & 3;
-      auto v_off = [&](int key, int d) { return 2 * kTensorBytes + qkv_off(key, d >> 3) + ((d & 4) << 1); };
-      floatx4 O[4], L;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const short4_t a4 = lds_tr(smem, v_off(128 + 4 * g4 + e, dbase(t, qd)));
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, __builtin_bit_cast(short4_t, Pt),
-                                                         floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        WATTN_PIN_MFMA();
-      }
-      {
-        const u32x2 ones2 = u32x2{0x3F803F80u, 0x3F803F80u};
-        L = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones2),
-                                                      __builtin_bit_cast(short4_t, Pt),
-                                                      floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        WATTN_PIN_MFMA();
-      }
-      // V^T fragments of key step j + 1 are read while step j runs
-      u32x4 vf[2][4];
-      auto vread = [&](int j, int buf) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const short4_t lo = lds_tr(smem, v_off(32 * j + 4 * g4 + e, dbase(t, qd)));
-          const short4_t hi = lds_tr(smem, v_off(32 * j + 16 + 4 * g4 + e, dbase(t, qd)));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          vf[buf][t] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-        }
-      };
-      vread(0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j + 1 < 4) vread(j + 1, (j + 1) & 1);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
-          WATTN_PIN_MFMA_LDS();
-        }
-        L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[j], L, 0, 0, 0);
-        WATTN_PIN_MFMA_LDS();
-      }
-
-      // ---- scatter O rows straight to grid layout (padding rows are cropped) ----
-      // The tile goes through its own Q rows in LDS (no longer needed) so that
-      // each store instruction writes eight whole 128-byte rows.
-      {
-        const float inv = __builtin_amdgcn_rcpf(L[0]);
-        const int r = qt * 16 + l16;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int d = dbase(t, g4);
-          const u32x2 w = u32x2{pack_bf16x2(O[t][0] * inv, O[t][1] * inv), pack_bf16x2(O[t][2] * inv, O[t][3] * inv)};
-          *reinterpret_cast<u32x2*>(smem + qkv_off(r, d >> 3) + ((d & 4) << 1)) = w;
-        }
-        const int rr = lane >> 3, cc = lane & 7;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = qt * 16 + 8 * h + rr;
-          const u32x4 w = *reinterpret_cast<const u32x4*>(smem + qkv_off(row, cc));
-          const int32_t tq = tokS[row];
-          if (tq >= 0) *reinterpret_cast<u32x4*>(o + (size_t)tq * RS + hoff + cc * 8) = w;
-        }
-      }
-    }
-    __syncthreads();  // LDS is free for the next item
-    if (!has_next) break;
-    new_window = next_win != win;
-    item = next;
-    win = next_win;
-    cur = nxt;
-    ++rot;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Non-persistent variant: one workgroup per (window, head) item, dispatched
-// head-major (item = head * n_windows + window), WAVES5 waves. K, V, mask
-// features and the slot table live in LDS; each wave loads the Q operands of
-// its own query tiles straight into registers.
-// ---------------------------------------------------------------------------
-#ifndef WAVES5
-#define WAVES5 4
-#endif
-#ifndef ORDER5
-#define ORDER5 0
-#endif
-constexpr int kThreads5 = 64 * WAVES5;
-// mask-feature table: the A fragment (8 bf16) of a key depends only on its
-// region code (0..7, or 8 for padding) and on the lane's 8-dim group (0..3)
-constexpr int kXt5 = 2 * kTensorBytes;
-constexpr int kCode5 = kXt5 + 9 * 4 * 16;
-constexpr int kTok5 = kCode5 + kN;
-constexpr int kSmem5 = kTok5 + kN * 4;
-
-__global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) void wattn_bf16_item(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, const PParams p) {
-  __shared__ __align__(16) uint8_t smem[kSmem5];
-  uint8_t* codeS = smem + kCode5;
-  int32_t* tokS = reinterpret_cast<int32_t*>(smem + kTok5);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -638,19 +350,14 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
   const size_t RS = (size_t)heads * 64;
   const int n_windows = p.n_items / heads;
   const int item = blockIdx.x;
-#if ORDER5 == 1
-  const int win = item / heads;
-  const int head = item - win * heads;
-#else
   const int head = item / n_windows;
   const int win = item - head * n_windows;
-#endif
   const WinPos cur = decode_window(p, win);
   const size_t hoff = (size_t)head * 64;
 
   // ---- slot table of the window ----
   uint32_t mycode = kPadCode;
-  for (int r = tid; r < kN; r += kThreads5) {
+  for (int r = tid; r < kN; r += kThreads) {
     int32_t t;
     map_slot(p, cur, p.slot[r], t, mycode);
     tokS[r] = t;
@@ -660,11 +367,11 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
 
   // ---- gather: K and V rows into registers, Q operands of this wave's tiles ----
   constexpr int kChunks = kN * 8;
-  constexpr int kPer = (kChunks + kThreads5 - 1) / kThreads5;
+  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
   u32x4 kr[kPer], vr[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int c = tid + kThreads5 * j;
+    const int c = tid + kThreads * j;
     kr[j] = vr[j] = u32x4{0, 0, 0, 0};
     if (c < kChunks) {
       const int32_t t = tokS[c >> 3];
@@ -675,11 +382,10 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
       }
     }
   }
-  constexpr int kMaxQT = (kNT + WAVES5 - 1) / WAVES5;
   u32x4 qr[kMaxQT][2];
 #pragma unroll
   for (int qi = 0; qi < kMaxQT; ++qi) {
-    const int qt = wave + WAVES5 * qi;
+    const int qt = wave + kWaves * qi;
     qr[qi][0] = qr[qi][1] = u32x4{0, 0, 0, 0};
     if (qt < kNT) {
       const int32_t t = tokS[qt * 16 + l16];
@@ -706,11 +412,11 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
         w[e] = lo | (hi << 16);
       }
     }
-    *reinterpret_cast<u32x4*>(smem + kXt5 + tid * 16) = w;
+    *reinterpret_cast<u32x4*>(smem + kXtOff + tid * 16) = w;
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int c = tid + kThreads5 * j;
+    const int c = tid + kThreads * j;
     if (c < kChunks) {
       *reinterpret_cast<u32x4*>(smem + qkv_off(c >> 3, c & 7)) = kr[j];
       *reinterpret_cast<u32x4*>(smem + kTensorBytes + qkv_off(c >> 3, c & 7)) = vr[j];
@@ -722,7 +428,7 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
   const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int qi = 0; qi < kMaxQT; ++qi) {
-    const int qt = wave + WAVES5 * qi;
+    const int qt = wave + kWaves * qi;
     if (qt >= kNT) break;
     const bf16x8_t qop[2] = {__builtin_bit_cast(bf16x8_t, qr[qi][0]), __builtin_bit_cast(bf16x8_t, qr[qi][1])};
 
@@ -762,7 +468,7 @@ __global__ __launch_bounds__(kThreads5) __attribute__((amdgpu_waves_per_eu(4))) 
       for (int kt = 0; kt < kNT; ++kt) {
         const uint32_t ck = codeS[kt * 16 + l16];
         const uint32_t row = ck == kPadCode ? 8u : ck;
-        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kXt5 + (row * 4 + g4) * 16);
+        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kXtOff + (row * 4 + g4) * 16);
       }
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt) {
@@ -887,24 +593,9 @@ hipError_t launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, 
                          dim3(p->threads), args, f32_lds_bytes(p->N, DH), s);
 }
 
-// Workgroups resident per CU for the bf16 kernel (LDS and registers allow two).
-constexpr int kBf16WgPerCu = 2;
-
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
                        hipStream_t s) {
-  PParams p;
+  AttnParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
   p.X[0] = d.D;
   p.X[1] = d.H;
@@ -928,15 +619,8 @@ hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-#ifdef WATTN_PERSISTENT
-  int64_t grid = (int64_t)cu_count() * kBf16WgPerCu;
-  if (grid > pl->n_items) grid = pl->n_items;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_n144_d64), dim3((unsigned)grid),
-                         dim3(kThreads), args, 0, s);
-#else
   return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_item), dim3((unsigned)pl->n_items),
-                         dim3(kThreads5), args, 0, s);
-#endif
+                         dim3(kThreads), args, 0, s);
 }
 
 }  // namespace
