@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "window-attention tokens/s at 0.25° stage-1 shape; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
-KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "wattn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wattn_bf16_stage1.json")
 
 
@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-ms", type=float, default=300.0, help="minimum warm-up time on the GPU")
     ap.add_argument("--bias", type=float, default=-100.0)
+    ap.add_argument("--workload", default="stage1",
+                    help="stage1 (default, the headline line) or another bf16 parity workload: "
+                         "stage2, stage2_s0, stage3_pad, stress_hres")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -145,7 +148,10 @@ def main():
     import datagen
     import swin3d_window_attention_amd as sw
 
-    wl = datagen.WORKLOADS["stage1"]
+    wl = datagen.WORKLOADS[args.workload]
+    if wl.dtype != "bf16":
+        sys.exit(f"bench.py: workload {wl.name} is a {wl.dtype} parity case, not a benchmark")
+    headline = wl.name == "stage1"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] inputs {wl.shape} {wl.dtype}")
@@ -190,7 +196,7 @@ def main():
     frac_mfma = tflops / BF16_MFMA_PEAK_TFLOPS
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         log("[bench] timing the fp64 oracle on the host")
         cpu = cpu_baseline(wl, args.cpu_budget)
 
@@ -208,7 +214,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded iid N(0,1) rounded to bf16)",
         "config": {
-            "workload": "0.25-degree stage-1-like window attention",
+            "workload": ("0.25-degree stage-1-like window attention" if headline
+                         else f"{wl.name} window attention"),
             "B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
             "window": list(wl.window), "shift": list(wl.shift), "cross_region_bias": args.bias,
             "tokens": wl.tokens, "windows": nwin, "masked_windows": info.n_masked_windows,
@@ -219,7 +226,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": frac_hbm,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if headline else None,
         },
         "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": frac_mfma},
         "algorithmic_bytes_per_launch": nbytes,

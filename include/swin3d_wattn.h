@@ -29,7 +29,10 @@
  * Precision: bf16 I/O uses bf16 matrix-core products for Q K^T and P V with
  * FP32 accumulation and an FP32 softmax; P is rounded to bf16 (nearest-even)
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
- * computes everything in FP32.
+ * computes everything in FP32. The bf16 kernel fills the padding slots of a
+ * window with the nearest real token and gives them a zero weight, so Q, K
+ * and V must be finite: an Inf or NaN there may also reach the windows that
+ * border the padding.
  *
  * Ownership: the caller owns every device buffer. The library allocates no
  * device memory; a plan is a small immutable host object.
@@ -76,7 +79,7 @@ typedef struct {
 typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 
 /* Validate *desc and build a plan. Host-only: no device is touched.
- * Supported: dtype BF16 with head_dim 64 and wd*wh*ww = 144; dtype F32 with
+ * Supported: dtype BF16 with head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with
  * head_dim 32 or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */

@@ -37,18 +37,25 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def kernel_sources():
+    """Every HIP source of the library, one kernel family per file."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source, link the shared library, and return its path."""
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     api_o = os.path.join(BUILD, "api.o")
-    ker_o = os.path.join(BUILD, "kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC, "-c",
           os.path.join(CSRC, "api.cpp"), "-o", api_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "kernels.hip"),
-          "-o", ker_o], verbose)
+    objs = [api_o]
+    for src in kernel_sources():
+        obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, ker_o, "-o", tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

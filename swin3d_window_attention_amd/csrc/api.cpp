@@ -85,7 +85,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   int32_t kernel = -1, threads = 0;
   if (d.dtype == SWIN3D_WATTN_BF16) {
-    if (d.head_dim == 64 && N == 144) { kernel = 1; threads = 256; }
+    // the launch grid is (window, head); its second dimension stays below 2^16
+    if (d.head_dim == 64 && N == 144 && d.heads < 65536) { kernel = 1; threads = 256; }
   } else {
     if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
       kernel = 0;
@@ -153,7 +154,6 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   p->c2 = (float)((double)d.scale * kLog2e);
   p->bias2 = std::isinf(d.cross_region_bias) ? -INFINITY
                                              : (float)((double)d.cross_region_bias * kLog2e);
-  p->n_items = n_windows * d.heads;
   // bias / scale as three bf16 terms (exact to ~2^-24 relative); anything at or
   // beyond -2^100 excludes, like -inf: its exponential is exactly zero
   const double big = -0x1p100;
@@ -222,5 +222,7 @@ extern "C" int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* 
   const int64_t bytes = plan->elems * plan->elem_bytes;
   if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
     return SWIN3D_WATTN_EINVAL;
-  return swin3d_wattn_launch(plan, q, k, v, o, stream);
+  const int e = plan->kernel == 1 ? wattn_launch_bf16(plan, q, k, v, o, stream)
+                                  : wattn_launch_f32(plan, q, k, v, o, stream);
+  return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }

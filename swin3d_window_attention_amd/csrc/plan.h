@@ -15,9 +15,8 @@ struct swin3d_wattn_plan {
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
   int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA
-  int64_t workgroups;       // for kernel 1: an upper bound, the launch uses min(items, 2 per CU)
-  int32_t threads;
-  int64_t n_items;          // n_windows * heads
+  int64_t workgroups;       // workgroups one run launches
+  int32_t threads;          // threads per workgroup
   float c2;                 // scale * log2(e)
   float bias2;              // cross_region_bias * log2(e)
   // bf16 kernel: the cross-region bias divided by scale, split into three
@@ -31,6 +30,10 @@ struct swin3d_wattn_plan {
   uint32_t slot[256];
 };
 
-// Defined in kernels.hip. Launches the plan's kernel; returns a swin3d code.
-int swin3d_wattn_launch(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v,
-                        void* o, void* stream);
+// Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip).
+// Each launches its kernel for the plan on `stream` (a hipStream_t) and
+// returns the HIP runtime's status (0 = success).
+int wattn_launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                     void* stream);
+int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                      void* stream);

@@ -1,4 +1,5 @@
-// Swin3D shifted-window attention kernels for gfx950 (MI355X).
+// Swin3D shifted-window attention kernel, BF16 I/O on the matrix cores, for gfx950
+// (MI355X).
 //
 // One workgroup computes one (window, head): it locates the window's tokens
 // in grid layout with an integer index map (pad, cyclic shift and 3D window
@@ -12,183 +13,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-
 #include "plan.h"
 
 namespace {
-
-struct Geom {
-  int32_t X[3];      // real extents D, H, W
-  int32_t P[3];      // padded extents
-  int32_t win[3];    // window
-  int32_t shift[3];  // cyclic shift
-  int32_t nwin[3];   // windows per axis
-  int32_t heads;
-  int32_t N;         // tokens per window
-  float scale;       // f32 kernel: natural-log units
-  float bias;
-  float c2;          // bf16 kernel: scale * log2(e)
-  float bias2;       // cross-region bias * log2(e)
-};
-
-constexpr uint32_t kPadCode = 0xFFu;
-
-// Index map of one window slot. Slot n = (od, oh, ow) row-major inside window
-// (kd, kh, kw); its shifted position is p = k * w + o, which holds grid
-// position g = (p + s) mod P (p + s < 2P, so one conditional subtract).
-// g >= X on any axis is padding. The region code has one bit per axis: set
-// when that axis is shifted and p lies in the wrapped part [P - s, P).
-__device__ __forceinline__ void slot_map(const Geom& g, int b, int kd, int kh, int kw, int n,
-                                         int32_t& tok, uint32_t& code) {
-  const int whw = g.win[1] * g.win[2];
-  const int od = n / whw;
-  const int r = n - od * whw;
-  const int oh = r / g.win[2];
-  const int ow = r - oh * g.win[2];
-  const int p0 = kd * g.win[0] + od, p1 = kh * g.win[1] + oh, p2 = kw * g.win[2] + ow;
-  int g0 = p0 + g.shift[0];
-  if (g0 >= g.P[0]) g0 -= g.P[0];
-  int g1 = p1 + g.shift[1];
-  if (g1 >= g.P[1]) g1 -= g.P[1];
-  int g2 = p2 + g.shift[2];
-  if (g2 >= g.P[2]) g2 -= g.P[2];
-  const bool valid = g0 < g.X[0] && g1 < g.X[1] && g2 < g.X[2];
-  uint32_t c = 0;
-  c |= (g.shift[0] > 0 && p0 >= g.P[0] - g.shift[0]) ? 1u : 0u;
-  c |= (g.shift[1] > 0 && p1 >= g.P[1] - g.shift[1]) ? 2u : 0u;
-  c |= (g.shift[2] > 0 && p2 >= g.P[2] - g.shift[2]) ? 4u : 0u;
-  code = valid ? c : kPadCode;
-  tok = valid ? ((b * g.X[0] + g0) * g.X[1] + g1) * g.X[2] + g2 : -1;
-}
-
-// blockIdx.x = window * heads + head, windows numbered (b, kd, kh, kw) row-major:
-// neighbouring workgroups read the other heads of the same tokens.
-__device__ __forceinline__ void decode_item(const Geom& g, int item, int& b, int& kd, int& kh,
-                                            int& kw, int& head) {
-  head = item % g.heads;
-  int w = item / g.heads;
-  const int per_b = g.nwin[0] * g.nwin[1] * g.nwin[2];
-  b = w / per_b;
-  w -= b * per_b;
-  kd = w / (g.nwin[1] * g.nwin[2]);
-  w -= kd * (g.nwin[1] * g.nwin[2]);
-  kh = w / g.nwin[2];
-  kw = w - kh * g.nwin[2];
-}
-
-// ---------------------------------------------------------------------------
-// FP32 path: vector-ALU kernel, one thread per query slot. K and V of the
-// window sit in LDS; every thread reads the same key row at the same time
-// (an LDS broadcast). Two passes over the keys: row max, then exp / sum / PV.
-// ---------------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict__ q,
-                                                        const float* __restrict__ k,
-                                                        const float* __restrict__ v,
-                                                        float* __restrict__ o, Geom g) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* Ks = reinterpret_cast<float*>(smem);
-  float* Vs = Ks + g.N * DH;
-  int32_t* tokS = reinterpret_cast<int32_t*>(Vs + g.N * DH);
-  uint32_t* codeS = reinterpret_cast<uint32_t*>(tokS + g.N);
-
-  int b, kd, kh, kw, head;
-  decode_item(g, blockIdx.x, b, kd, kh, kw, head);
-  const int tid = threadIdx.x;
-  for (int n = tid; n < g.N; n += blockDim.x) {
-    int32_t t;
-    uint32_t c;
-    slot_map(g, b, kd, kh, kw, n, t, c);
-    tokS[n] = t;
-    codeS[n] = c;
-  }
-  __syncthreads();
-
-  const size_t RS = (size_t)g.heads * DH;
-  const size_t hoff = (size_t)head * DH;
-  constexpr int C = DH / 4;
-  for (int idx = tid; idx < g.N * C; idx += blockDim.x) {
-    const int n = idx / C, c = idx - n * C;
-    const int32_t t = tokS[n];
-    float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
-    if (t >= 0) {
-      const size_t off = (size_t)t * RS + hoff + 4 * c;
-      kk = *reinterpret_cast<const float4*>(k + off);
-      vv = *reinterpret_cast<const float4*>(v + off);
-    }
-    *reinterpret_cast<float4*>(Ks + n * DH + 4 * c) = kk;
-    *reinterpret_cast<float4*>(Vs + n * DH + 4 * c) = vv;
-  }
-  __syncthreads();
-
-  const int n = tid;
-  if (n >= g.N) return;
-  const int32_t t = tokS[n];
-  if (t < 0) return;  // padding query: cropped, never written
-  const uint32_t cq = codeS[n];
-  const size_t qoff = (size_t)t * RS + hoff;
-
-  float qr[DH];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const float4 x = *reinterpret_cast<const float4*>(q + qoff + 4 * c);
-    qr[4 * c] = x.x;
-    qr[4 * c + 1] = x.y;
-    qr[4 * c + 2] = x.z;
-    qr[4 * c + 3] = x.w;
-  }
-
-  auto logit = [&](int j) -> float {
-    const float* kr = Ks + j * DH;
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float4 x = *reinterpret_cast<const float4*>(kr + 4 * c);
-      s = fmaf(qr[4 * c], x.x, s);
-      s = fmaf(qr[4 * c + 1], x.y, s);
-      s = fmaf(qr[4 * c + 2], x.z, s);
-      s = fmaf(qr[4 * c + 3], x.w, s);
-    }
-    const uint32_t ck = codeS[j];
-    const float add = (ck == kPadCode) ? -INFINITY : (ck != cq ? g.bias : 0.f);
-    return fmaf(s, g.scale, add);
-  };
-
-  float m = -INFINITY;
-  for (int j = 0; j < g.N; ++j) m = fmaxf(m, logit(j));
-
-  float acc[DH];
-#pragma unroll
-  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
-  float l = 0.f;
-  for (int j = 0; j < g.N; ++j) {
-    const float p = expf(logit(j) - m);
-    l += p;
-    const float* vr = Vs + j * DH;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float4 x = *reinterpret_cast<const float4*>(vr + 4 * c);
-      acc[4 * c] = fmaf(p, x.x, acc[4 * c]);
-      acc[4 * c + 1] = fmaf(p, x.y, acc[4 * c + 1]);
-      acc[4 * c + 2] = fmaf(p, x.z, acc[4 * c + 2]);
-      acc[4 * c + 3] = fmaf(p, x.w, acc[4 * c + 3]);
-    }
-  }
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    *reinterpret_cast<float4*>(o + qoff + 4 * c) =
-        make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // BF16 path: matrix-core kernel for N = 144 tokens per window (window
 // (2, 6, 12) or any other with 144 slots) and head_dim 64.
 //
-// Work: one workgroup of four waves per (window, head) item, dispatched
-// head-major (item = head * n_windows + window): the workgroups in flight
+// Work: one workgroup of four waves per (window, head) item, launch grid
+// (window, head) so that dispatch is head-major: the workgroups in flight
 // read one head of many neighbouring windows, the order HBM serves best for
 // these 128-byte rows. Small workgroups (38 KB of LDS, <= 128 VGPRs) let four
 // of them share a CU, so one workgroup's loads overlap another's math.
@@ -239,18 +73,39 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxQT = (kNT + kWaves - 1) / kWaves;  // query tiles per wave (at most)
 constexpr int kTensorBytes = kN * 128;    // one 144 x 64 bf16 tile
-// LDS layout (bytes): K tile, V tile, mask-feature table (9 codes x 4
-// groups x 16 B; code 8 = padding), region code and token of each slot
+constexpr uint32_t kPadSlot = 8;          // region code of a padding slot
+// LDS layout (bytes): K tile, V tile, the key and the query mask-feature
+// tables (9 codes x 4 lane groups x 16 B each), then the region code and
+// the token of each slot
 constexpr int kXtOff = 2 * kTensorBytes;
-constexpr int kCodeOff = kXtOff + 9 * 4 * 16;
+constexpr int kQtOff = kXtOff + 9 * 4 * 16;
+constexpr int kCodeOff = kQtOff + 9 * 4 * 16;
 constexpr int kTokOff = kCodeOff + kN;
 constexpr int kSmemBytes = kTokOff + kN * 4;
+
+// floor(n / d) for 0 <= n < 2^31 as (n * mul) >> shr: with l = ceil(log2 d),
+// shr = 31 + l and mul = ceil(2^shr / d), the product error stays below one
+// step of n (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, Theorem 4.2 with N = 31)
+struct FastDiv {
+  uint32_t mul, shr;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint32_t shr = 31 + l;
+  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
+}
 
 struct AttnParams {
   int32_t X[3], P[3], shift[3], win[3], nwin[3];
   int32_t special[3][3];
-  int32_t heads;
-  int32_t n_items;
+  FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
   float c2;
   uint32_t beta01;  // bf16 beta term 0 | term 1 << 16
   uint32_t beta2;   // bf16 beta term 2
@@ -279,15 +134,15 @@ struct WinPos {
 
 // Window w (batch folded in) -> (b, kd, kh, kw) and whether it needs the
 // mask path (a region cut or padding along some axis).
-__device__ __forceinline__ WinPos decode_window(const AttnParams& p, int w) {
+__device__ __forceinline__ WinPos decode_window(const AttnParams& p, uint32_t w) {
   WinPos it;
-  const int per_b = p.nwin[0] * p.nwin[1] * p.nwin[2];
-  it.b = w / per_b;
-  w -= it.b * per_b;
-  it.k[0] = w / (p.nwin[1] * p.nwin[2]);
-  w -= it.k[0] * (p.nwin[1] * p.nwin[2]);
-  it.k[1] = w / p.nwin[2];
-  it.k[2] = w - it.k[1] * p.nwin[2];
+  const uint32_t per_d = (uint32_t)(p.nwin[1] * p.nwin[2]);
+  it.b = (int)fdiv(w, p.div_b);
+  w -= (uint32_t)it.b * per_d * (uint32_t)p.nwin[0];
+  it.k[0] = (int)fdiv(w, p.div_d);
+  w -= (uint32_t)it.k[0] * per_d;
+  it.k[1] = (int)fdiv(w, p.div_h);
+  it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
   bool m = false;
 #pragma unroll
   for (int a = 0; a < 3; ++a)
@@ -297,9 +152,11 @@ __device__ __forceinline__ WinPos decode_window(const AttnParams& p, int w) {
   return it;
 }
 
-// Grid position of slot (od, oh, ow) of a window: token index, or -1 for
-// padding, and the region code (one bit per axis: shifted axis and position
-// in the wrapped part [P - s, P)).
+// Grid position of slot (od, oh, ow) of a window and its region code (one
+// bit per axis: shifted axis and position in the wrapped part [P - s, P)),
+// or kPadSlot for padding. A padding slot still gets a real token, the
+// nearest one on the grid (each coordinate clamped to X - 1), so that all
+// loads can be unconditional.
 __device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, uint32_t packed, int32_t& tok,
                                          uint32_t& code) {
   const int o[3] = {(int)(packed & 0xFF), (int)((packed >> 8) & 0xFF), (int)(packed >> 16)};
@@ -311,12 +168,12 @@ __device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, 
     const int pa = it.k[a] * p.win[a] + o[a];
     int ga = pa + p.shift[a];
     ga = ga >= p.P[a] ? ga - p.P[a] : ga;
-    g[a] = ga;
     valid = valid && ga < p.X[a];
+    g[a] = min(ga, p.X[a] - 1);
     c |= (p.shift[a] > 0 && pa >= p.P[a] - p.shift[a]) ? (1u << a) : 0u;
   }
-  tok = valid ? ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2] : -1;
-  code = valid ? c : kPadCode;
+  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
+  code = valid ? c : kPadSlot;
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) { return *reinterpret_cast<const u32x4*>(ptr); }
@@ -346,73 +203,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
-  const int heads = p.heads;
-  const size_t RS = (size_t)heads * 64;
-  const int n_windows = p.n_items / heads;
-  const int item = blockIdx.x;
-  const int head = item / n_windows;
-  const int win = item - head * n_windows;
-  const WinPos cur = decode_window(p, win);
+  // grid (window, head): x varies fastest, so the workgroups in flight read
+  // one head of many neighbouring windows
+  const size_t RS = (size_t)gridDim.y * 64;
+  const int head = blockIdx.y;
+  const WinPos cur = decode_window(p, blockIdx.x);
   const size_t hoff = (size_t)head * 64;
 
   // ---- slot table of the window ----
-  uint32_t mycode = kPadCode;
   for (int r = tid; r < kN; r += kThreads) {
     int32_t t;
-    map_slot(p, cur, p.slot[r], t, mycode);
+    uint32_t c;
+    map_slot(p, cur, p.slot[r], t, c);
     tokS[r] = t;
-    codeS[r] = (uint8_t)mycode;
+    codeS[r] = (uint8_t)c;
+  }
+  // ---- mask-feature tables (windows with a cut or padding only), built by
+  // the wave that has no slots to map ----
+  if (cur.masked && tid >= kThreads - 64) {
+    for (int e = tid - (kThreads - 64); e < 72; e += 64) {
+      const uint32_t ck = (e < 36 ? e : e - 36) >> 2, part = e & 3;
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (e < 36) {
+        // key: bias / scale at every region other than its own (three bf16
+        // terms, parts 0..2), the padding offset in the padding column (part 3)
+        const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
+        if (ck == kPadSlot) {
+          if (part == 3) w[0] = p.pad;
+        } else if (part < 3) {
+          const uint32_t bt = beta[part];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (uint32_t)(2 * i) != ck ? bt : 0u;
+            const uint32_t hi = (uint32_t)(2 * i + 1) != ck ? bt : 0u;
+            w[i] = lo | (hi << 16);
+          }
+        }
+      } else if (part < 3) {
+        // query: a one-hot of its region in each of the three slots
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = ((uint32_t)(2 * i) == ck ? 0x3F80u : 0u) | ((uint32_t)(2 * i + 1) == ck ? 0x3F800000u : 0u);
+      } else {
+        w[0] = 0x3F80u;  // query: 1 in the padding column
+      }
+      *reinterpret_cast<u32x4*>(smem + kXtOff + e * 16) = w;
+    }
   }
   __syncthreads();
 
-  // ---- gather: K and V rows into registers, Q operands of this wave's tiles ----
+  // ---- gather: K and V rows into registers, Q operands of this wave's tiles.
+  // Padding slots read their stand-in token: a padding key gets a zero weight
+  // and a padding query is never written, so any finite value will do. ----
   constexpr int kChunks = kN * 8;
   constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
   u32x4 kr[kPer], vr[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;
-    kr[j] = vr[j] = u32x4{0, 0, 0, 0};
     if (c < kChunks) {
-      const int32_t t = tokS[c >> 3];
-      if (t >= 0) {
-        const size_t off = (size_t)t * RS + hoff + (c & 7) * 8;
-        kr[j] = ldg16(k + off);
-        vr[j] = ldg16(v + off);
-      }
+      const size_t off = (size_t)tokS[c >> 3] * RS + hoff + (c & 7) * 8;
+      kr[j] = ldg16(k + off);
+      vr[j] = ldg16(v + off);
     }
   }
   u32x4 qr[kMaxQT][2];
 #pragma unroll
   for (int qi = 0; qi < kMaxQT; ++qi) {
     const int qt = wave + kWaves * qi;
-    qr[qi][0] = qr[qi][1] = u32x4{0, 0, 0, 0};
     if (qt < kNT) {
-      const int32_t t = tokS[qt * 16 + l16];
-      if (t >= 0) {
-        const size_t off = (size_t)t * RS + hoff + 8 * g4;
-        qr[qi][0] = ldg16(q + off);
-        qr[qi][1] = ldg16(q + off + 32);
-      }
+      const size_t off = (size_t)tokS[qt * 16 + l16] * RS + hoff + 8 * g4;
+      qr[qi][0] = ldg16(q + off);
+      qr[qi][1] = ldg16(q + off + 32);
     }
-  }
-  // mask-feature table (only windows with a cut or padding use it)
-  if (cur.masked && tid < 36) {
-    const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
-    const uint32_t ck = tid >> 2, part = tid & 3;  // ck == 8: padding key
-    u32x4 w = u32x4{0, 0, 0, 0};
-    if (ck == 8) {
-      if (part == 3) w[0] = p.pad;
-    } else if (part < 3) {
-      const uint32_t bt = beta[part];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (uint32_t)(2 * e) != ck ? bt : 0u;
-        const uint32_t hi = (uint32_t)(2 * e + 1) != ck ? bt : 0u;
-        w[e] = lo | (hi << 16);
-      }
-    }
-    *reinterpret_cast<u32x4*>(smem + kXtOff + tid * 16) = w;
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -453,23 +316,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
     }
     if (cur.masked) {
-      const uint32_t cq = codeS[qt * 16 + l16];
-      u32x4 qx = u32x4{0, 0, 0, 0};
-      if (g4 < 3) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          qx[e] = (cq == (uint32_t)(2 * e) ? 0x3F80u : 0u) | (cq == (uint32_t)(2 * e + 1) ? 0x3F800000u : 0u);
-      } else {
-        qx[0] = 0x3F80u;
-      }
-      const bf16x8_t qxb = __builtin_bit_cast(bf16x8_t, qx);
+      const bf16x8_t qxb =
+          *reinterpret_cast<const bf16x8_t*>(smem + kQtOff + (codeS[qt * 16 + l16] * 4 + g4) * 16);
       bf16x8_t xf[kNT];
 #pragma unroll
-      for (int kt = 0; kt < kNT; ++kt) {
-        const uint32_t ck = codeS[kt * 16 + l16];
-        const uint32_t row = ck == kPadCode ? 8u : ck;
-        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kXtOff + (row * 4 + g4) * 16);
-      }
+      for (int kt = 0; kt < kNT; ++kt)
+        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + kXtOff + (codeS[kt * 16 + l16] * 4 + g4) * 16);
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt) {
         S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
@@ -536,10 +388,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       WATTN_PIN_MFMA_LDS();
     }
 
-    const int32_t tq = tokS[qt * 16 + l16];
-    if (tq >= 0) {
+    if (codeS[qt * 16 + l16] != kPadSlot) {
       const float inv = __builtin_amdgcn_rcpf(L[0]);
-      uint16_t* out = o + (size_t)tq * RS + hoff;
+      uint16_t* out = o + (size_t)tokS[qt * 16 + l16] * RS + hoff;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const u32x2 w = u32x2{pack_bf16x2(O[t][0] * inv, O[t][1] * inv), pack_bf16x2(O[t][2] * inv, O[t][3] * inv)};
@@ -549,51 +400,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-Geom make_geom(const swin3d_wattn_plan* p) {
-  Geom g;
-  const swin3d_wattn_desc_t& d = p->desc;
-  g.X[0] = d.D;
-  g.X[1] = d.H;
-  g.X[2] = d.W;
-  for (int a = 0; a < 3; ++a) {
-    g.P[a] = p->padded[a];
-    g.win[a] = d.window[a];
-    g.shift[a] = d.shift[a];
-    g.nwin[a] = p->nwin[a];
-  }
-  g.heads = d.heads;
-  g.N = p->N;
-  g.scale = d.scale;
-  g.bias = d.cross_region_bias;
-  g.c2 = p->c2;
-  g.bias2 = p->bias2;
-  return g;
-}
-
-size_t f32_lds_bytes(int N, int dh) { return (size_t)N * dh * 4 * 2 + (size_t)N * 8; }
-
-template <int DH>
-hipError_t launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                      hipStream_t s) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&wattn_f32_kernel<DH>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)f32_lds_bytes(256, DH));
-  });
-  if (attr_err != hipSuccess) return attr_err;
-  Geom g = make_geom(p);
-  const float* qq = static_cast<const float*>(q);
-  const float* kk = static_cast<const float*>(k);
-  const float* vv = static_cast<const float*>(v);
-  float* oo = static_cast<float*>(o);
-  void* args[] = {&qq, &kk, &vv, &oo, &g};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_f32_kernel<DH>), dim3((unsigned)p->workgroups),
-                         dim3(p->threads), args, f32_lds_bytes(p->N, DH), s);
-}
-
-hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
                        hipStream_t s) {
   AttnParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
@@ -607,8 +414,9 @@ hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k
     p.nwin[a] = pl->nwin[a];
     for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
   }
-  p.heads = d.heads;
-  p.n_items = (int32_t)pl->n_items;
+  p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
+  p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
+  p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
   p.c2 = pl->c2;
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
@@ -619,22 +427,13 @@ hipError_t launch_bf16(const swin3d_wattn_plan* pl, const void* q, const void* k
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_item), dim3((unsigned)pl->n_items),
-                         dim3(kThreads), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_item),
+                         dim3((unsigned)pl->n_windows, (unsigned)d.heads), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace
 
-int swin3d_wattn_launch(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                        void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (p->kernel == 1) {
-    e = launch_bf16(p, q, k, v, o, s);
-  } else if (p->desc.head_dim == 32) {
-    e = launch_f32<32>(p, q, k, v, o, s);
-  } else {
-    e = launch_f32<64>(p, q, k, v, o, s);
-  }
-  return e == hipSuccess ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
+int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                      void* stream) {
+  return (int)launch(p, q, k, v, o, static_cast<hipStream_t>(stream));
 }

@@ -90,6 +90,7 @@ def test_masked_window_count_matches_oracle_labels():
     (dict(window=(4, 8, 12), shift=(1, 3, 3), dtype="f32", head_dim=64), -2),
     (dict(dtype="f32", head_dim=48), -2),
     (dict(B=2, D=4, H=46341, W=46341), -2),
+    (dict(D=1, H=1, W=1, heads=65536), -2),
 ])
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)
@@ -98,7 +99,7 @@ def test_create_rejects(kw, code):
 
 def test_create_accepts_edge_cases():
     for kw in [dict(cross_region_bias=-math.inf), dict(shift=(0, 0, 0)), dict(shift=(1, 5, 11)),
-               dict(D=1, H=1, W=1), dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)),
+               dict(D=1, H=1, W=1), dict(D=1, H=1, W=1, heads=65535), dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)),
                dict(dtype="f32", head_dim=64, window=(4, 8, 8), shift=(3, 7, 7))]:
         rc, h = _create(**kw)
         assert rc == 0, kw

@@ -16,7 +16,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc")
+SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 NEAR_MFMAS = 3      # a SrcC produced this many MFMAs back or fewer counts as "in flight"
 WINDOW_INSTRS = 40  # instructions after such an MFMA in which its A/B must not be rewritten
@@ -73,16 +74,21 @@ def stalled_mfma_war(instrs):
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
+    """gfx950 assembly of every kernel source, concatenated."""
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "kernels.s"
-    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.dirname(SRC), SRC, "-o", str(out)]
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    assert r.returncode == 0, r.stdout
-    return out.read_text()
+    tmp = tmp_path_factory.mktemp("isa")
+    text = []
+    for src in SOURCES:
+        out = tmp / (os.path.basename(src) + ".s")
+        cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", str(out)]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        assert r.returncode == 0, r.stdout
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 def test_scanner_flags_the_pattern():
@@ -110,3 +116,17 @@ def test_no_stalled_mfma_operand_overwrite(asm):
         total += n
         assert not hits, f"{name}: {len(hits)} risky overwrites, first: {hits[0]}"
     assert total > 0  # the matrix-core kernel was scanned
+
+
+def test_no_register_spills(asm):
+    """Every kernel keeps its registers: a spill to scratch makes the gather wait for all of its
+    loads before it can park them, which costs the bf16 kernel about a tenth of its speed."""
+    sizes = re.findall(r"\.amdhsa_kernel\s+(\S+).*?\.amdhsa_private_segment_fixed_size\s+(\d+)", asm, re.S)
+    assert sizes and any("wattn_bf16" in k for k, _ in sizes)
+    assert all(int(n) == 0 for _, n in sizes), sizes
+
+
+def test_bf16_kernel_occupancy(asm):
+    """Four workgroups of the matrix-core kernel share a CU (four waves per SIMD)."""
+    m = re.search(r"wattn_bf16_item\w*:.*?; Occupancy: (\d+)", asm, re.S)
+    assert m and int(m.group(1)) >= 4
