@@ -167,11 +167,6 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   p->pad_bf16 = bf16_rne(big);
   for (int a = 0; a < 3; ++a)
     for (int j = 0; j < 3; ++j) p->special[a][j] = special[a][j];
-  for (int32_t n = 0; n < N && n < 256; ++n) {
-    const int32_t whw = d.window[1] * d.window[2];
-    const int32_t od = n / whw, oh = (n % whw) / d.window[2], ow = n % d.window[2];
-    p->slot[n] = (uint32_t)od | ((uint32_t)oh << 8) | ((uint32_t)ow << 16);
-  }
   *out = p;
   return SWIN3D_WATTN_OK;
 }

@@ -26,8 +26,6 @@ struct swin3d_wattn_plan {
   uint16_t pad_bf16;
   // per axis: window indices that hold a region cut or padding (-1 = none)
   int32_t special[3][3];
-  // slot n of a window -> (od, oh, ow) packed as od | oh << 8 | ow << 16
-  uint32_t slot[256];
 };
 
 // Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip).
