@@ -129,6 +129,9 @@ def main():
                          "stage2, stage2_s0, stage3_pad, stress_hres")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="flush the 256 MB Infinity Cache (write a 1 GiB buffer) before every timed "
+                         "launch and time each launch with its own events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (profiler counter calibration)")
     args = ap.parse_args()
@@ -177,15 +180,29 @@ def main():
         extra += 20
     log(f"[bench] warmup {args.warmup} + {extra} steps done; timing {args.steps} steps")
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        plan.run(x["q"], x["k"], x["v"], o)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"[bench] {ms * 1000:.1f} us per step")
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s, e in evs:
+            flush.fill_(1)
+            s.record(stream)
+            plan.run(x["q"], x["k"], x["v"], o)
+            e.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(s.elapsed_time(e) for s, e in evs) / args.steps
+        del flush
+    else:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            plan.run(x["q"], x["k"], x["v"], o)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] {ms * 1000:.1f} us per step{' (cold cache)' if args.cold else ''}")
 
     nbytes, flops, nwin = algorithmic_work(wl)
     sec = ms / 1e3
@@ -219,6 +236,7 @@ def main():
             "B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
             "window": list(wl.window), "shift": list(wl.shift), "cross_region_bias": args.bias,
             "tokens": wl.tokens, "windows": nwin, "masked_windows": info.n_masked_windows,
+            "cache": "flushed before each launch" if args.cold else "warm (back-to-back launches)",
         },
         "roofline": {
             "bound": "hbm",

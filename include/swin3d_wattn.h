@@ -94,6 +94,35 @@ int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
 int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* k, const void* v, void* o,
                      void* stream);
 
+/* Token strides, in elements, of the four tensors for
+ * swin3d_wattn_run_strided: element (token t, head h, dim d) of Q sits at
+ * q[t * q + h * head_dim + d], and likewise for K, V and O, where token t
+ * runs over B*D*H*W in row-major [B, D, H, W] order. Within a token the
+ * heads * head_dim elements stay contiguous.
+ *
+ * This lets the path read Q, K and V straight out of a fused projection
+ * output [B, D, H, W, 3, heads, head_dim] (q = base, k = base + heads*head_dim,
+ * v = base + 2*heads*head_dim, all three strides 3*heads*head_dim) and write O
+ * into a wider buffer, so no copy is needed on either side of the attention
+ * (the layout-copy removal of the Flash-Aurora README, "Kernel fusion for
+ * backbone memory traffic"). Contiguous grid-layout tensors have stride
+ * heads*head_dim. */
+typedef struct {
+  int64_t q, k, v, o;
+} swin3d_wattn_strides_t;
+
+/* swin3d_wattn_run with explicit token strides (see swin3d_wattn_strides_t).
+ * Each stride must be >= heads*head_dim and a multiple of 16 bytes; the
+ * pointers 16-byte aligned. The span of a tensor is the byte range
+ * [ptr, ptr + ((tokens - 1) * stride + heads*head_dim) * element size); the
+ * span of O must not overlap the spans of Q, K or V, while Q, K and V may
+ * overlap each other. Elements of
+ * the O buffer outside the (token, head, dim) positions are never touched.
+ * Returns 0, EINVAL (null plan, pointer or strides, a stride too small or
+ * misaligned, misalignment, overlap) or ELAUNCH. */
+int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, const void* k, const void* v, void* o,
+                             const swin3d_wattn_strides_t* strides, void* stream);
+
 /* Release a plan. NULL is a no-op. Returns 0. */
 int swin3d_wattn_destroy(swin3d_wattn_t plan);
 

@@ -53,6 +53,11 @@ class Swin3dWattnInfo(ctypes.Structure):
     ]
 
 
+class Swin3dWattnStrides(ctypes.Structure):
+    """Token strides (elements) of Q, K, V, O: swin3d_wattn_strides_t."""
+    _fields_ = [("q", ctypes.c_int64), ("k", ctypes.c_int64), ("v", ctypes.c_int64), ("o", ctypes.c_int64)]
+
+
 class Swin3dWattnError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -81,6 +86,9 @@ def load_library():
         lib.swin3d_wattn_create.restype = ctypes.c_int
         lib.swin3d_wattn_run.argtypes = [ctypes.c_void_p] * 6
         lib.swin3d_wattn_run.restype = ctypes.c_int
+        lib.swin3d_wattn_run_strided.argtypes = [ctypes.c_void_p] * 5 + [ctypes.POINTER(Swin3dWattnStrides),
+                                                                         ctypes.c_void_p]
+        lib.swin3d_wattn_run_strided.restype = ctypes.c_int
         lib.swin3d_wattn_destroy.argtypes = [ctypes.c_void_p]
         lib.swin3d_wattn_destroy.restype = ctypes.c_int
         lib.swin3d_wattn_strerror.argtypes = [ctypes.c_int]
@@ -102,6 +110,11 @@ def swin3d_wattn_create(desc: Swin3dWattnDesc):
 
 def swin3d_wattn_run(plan, q: int, k: int, v: int, o: int, stream: int = 0) -> int:
     return load_library().swin3d_wattn_run(plan, q, k, v, o, stream)
+
+
+def swin3d_wattn_run_strided(plan, q: int, k: int, v: int, o: int, strides: Swin3dWattnStrides,
+                             stream: int = 0) -> int:
+    return load_library().swin3d_wattn_run_strided(plan, q, k, v, o, ctypes.byref(strides), stream)
 
 
 def swin3d_wattn_destroy(plan) -> int:
@@ -167,24 +180,54 @@ class Plan:
             raise Swin3dWattnError(rc, "swin3d_wattn_get_info")
         return info
 
+    def _token_stride(self, t) -> int:
+        """Elements between consecutive tokens of a [B, D, H, W, heads, head_dim] view whose
+        (heads, head_dim) block is contiguous and whose tokens are evenly spaced in row-major
+        [B, D, H, W] order (a contiguous tensor, or e.g. q/k/v slices of a fused QKV buffer)."""
+        heads, dh = self.shape[4], self.shape[5]
+        st = t.stride()
+        if (dh > 1 and st[5] != 1) or (heads > 1 and st[4] != dh):
+            raise ValueError("the (heads, head_dim) block of each token must be contiguous")
+        ts = None
+        span = 1
+        for axis in (3, 2, 1, 0):
+            if t.shape[axis] > 1:
+                if ts is None:
+                    ts = st[axis] // span if st[axis] % span == 0 else -1
+                if ts < 0 or st[axis] != ts * span:
+                    raise ValueError("tokens must be evenly spaced in [B, D, H, W] order")
+            span *= t.shape[axis]
+        return heads * dh if ts is None else ts
+
     def run(self, q, k, v, o, stream=None) -> None:
+        """O = attention(Q, K, V) on `stream` (default: torch's current stream). Q, K, V, O are
+        [B, D, H, W, heads, head_dim] device tensors: contiguous, or token-strided views."""
         import torch
 
+        strides = []
         for t in (q, k, v, o):
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("q, k, v, o must be contiguous device tensors")
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise ValueError("q, k, v, o must be device tensors")
             if tuple(t.shape) != self.shape:
                 raise ValueError(f"expected shape {self.shape}, got {tuple(t.shape)}")
             if _dtype_code(t.dtype) != self.desc.dtype:
                 raise ValueError("tensor dtype does not match the plan")
+            strides.append(self._token_stride(t))
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         elif isinstance(stream, torch.cuda.Stream):
             stream = stream.cuda_stream
-        rc = self._lib.swin3d_wattn_run(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                        stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+        row = self.shape[4] * self.shape[5]
+        if all(s == row for s in strides):
+            rc = self._lib.swin3d_wattn_run(self._h, *ptrs, stream)
+            where = "swin3d_wattn_run"
+        else:
+            rc = self._lib.swin3d_wattn_run_strided(self._h, *ptrs, ctypes.byref(Swin3dWattnStrides(*strides)),
+                                                    stream)
+            where = "swin3d_wattn_run_strided"
         if rc != SWIN3D_WATTN_OK:
-            raise Swin3dWattnError(rc, "swin3d_wattn_run")
+            raise Swin3dWattnError(rc, where)
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -203,21 +203,35 @@ extern "C" int swin3d_wattn_get_info(swin3d_wattn_t plan, swin3d_wattn_info_t* i
 }
 
 namespace {
-bool overlaps(const void* a, const void* b, int64_t bytes) {
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+  return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
 }
 bool misaligned(const void* a) { return ((uintptr_t)a & 15u) != 0; }
 }  // namespace
 
+extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, const void* k, const void* v,
+                                        void* o, const swin3d_wattn_strides_t* st, void* stream) {
+  if (!plan || !q || !k || !v || !o || !st) return SWIN3D_WATTN_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return SWIN3D_WATTN_EINVAL;
+  const int64_t row = (int64_t)plan->desc.heads * plan->desc.head_dim;  // elements per token
+  const int64_t s[4] = {st->q, st->k, st->v, st->o};
+  int64_t span[4];
+  for (int i = 0; i < 4; ++i) {
+    if (s[i] < row || s[i] > (int64_t(1) << 40) || (s[i] * plan->elem_bytes) % 16 != 0) return SWIN3D_WATTN_EINVAL;
+    span[i] = ((plan->tokens - 1) * s[i] + row) * plan->elem_bytes;
+  }
+  if (overlaps(o, span[3], q, span[0]) || overlaps(o, span[3], k, span[1]) || overlaps(o, span[3], v, span[2]))
+    return SWIN3D_WATTN_EINVAL;
+  const int e = plan->kernel == 1 ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
+                                  : wattn_launch_f32(plan, q, k, v, o, st, stream);
+  return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
+}
+
 extern "C" int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* k, const void* v,
                                 void* o, void* stream) {
-  if (!plan || !q || !k || !v || !o) return SWIN3D_WATTN_EINVAL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return SWIN3D_WATTN_EINVAL;
-  const int64_t bytes = plan->elems * plan->elem_bytes;
-  if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
-    return SWIN3D_WATTN_EINVAL;
-  const int e = plan->kernel == 1 ? wattn_launch_bf16(plan, q, k, v, o, stream)
-                                  : wattn_launch_f32(plan, q, k, v, o, stream);
-  return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
+  if (!plan) return SWIN3D_WATTN_EINVAL;
+  const int64_t row = (int64_t)plan->desc.heads * plan->desc.head_dim;
+  const swin3d_wattn_strides_t st = {row, row, row, row};
+  return swin3d_wattn_run_strided(plan, q, k, v, o, &st, stream);
 }

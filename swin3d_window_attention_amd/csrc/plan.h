@@ -30,8 +30,9 @@ struct swin3d_wattn_plan {
 
 // Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip).
 // Each launches its kernel for the plan on `stream` (a hipStream_t) and
-// returns the HIP runtime's status (0 = success).
+// returns the HIP runtime's status (0 = success). `stride` holds the token
+// strides of Q, K, V and O in elements, already validated.
 int wattn_launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                     void* stream);
+                     const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                      void* stream);
+                      const swin3d_wattn_strides_t* stride, void* stream);

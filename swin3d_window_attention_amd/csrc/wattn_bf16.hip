@@ -107,6 +107,7 @@ struct AttnParams {
   int32_t special[3][3];
   FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
   FastDiv div_hw, div_w;        // by window slots per depth step (wh * ww), per row (ww)
+  int64_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements)
   float c2;
   uint32_t beta01;  // bf16 beta term 0 | term 1 << 16
   uint32_t beta2;   // bf16 beta term 2
@@ -216,7 +217,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int l16 = lane & 15;
   // grid (window, head): x varies fastest, so the workgroups in flight read
   // one head of many neighbouring windows
-  const size_t RS = (size_t)gridDim.y * 64;
   const int head = blockIdx.y;
   const WinPos cur = decode_window(p, blockIdx.x);
   const size_t hoff = (size_t)head * 64;
@@ -236,9 +236,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       int32_t t;
       uint32_t unused;
       map_slot(p, cur, (uint32_t)(c >> 3), t, unused);
-      const size_t off = (size_t)t * RS + hoff + (c & 7) * 8;
-      kr[j] = ldg16(k + off);
-      vr[j] = ldg16(v + off);
+      kr[j] = ldg16(k + (size_t)t * p.sk + hoff + (c & 7) * 8);
+      vr[j] = ldg16(v + (size_t)t * p.sv + hoff + (c & 7) * 8);
     }
   }
   // Q rows of this wave's tiles are read whole: load s of a tile covers its
@@ -253,7 +252,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         int32_t t;
         uint32_t unused;
         map_slot(p, cur, (uint32_t)(qt * 16 + 8 * s + (lane >> 3)), t, unused);
-        qr[qi][s] = ldg16(q + (size_t)t * RS + hoff + 8 * (lane & 7));
+        qr[qi][s] = ldg16(q + (size_t)t * p.sq + hoff + 8 * (lane & 7));
       }
     }
   }
@@ -460,13 +459,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         val[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)(mine ? c0[d] : z[d]));
       const int r = qt * 16 + 8 * s + rr;
       if (codeS[r] != kPadSlot)
-        *reinterpret_cast<u32x4*>(o + (size_t)tokS[r] * RS + hoff + 8 * ch) = val;
+        *reinterpret_cast<u32x4*>(o + (size_t)tokS[r] * p.so + hoff + 8 * ch) = val;
     }
   }
 }
 
 hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
-                       hipStream_t s) {
+                  const swin3d_wattn_strides_t* st, hipStream_t s) {
   AttnParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
   p.X[0] = d.D;
@@ -486,6 +485,10 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
   p.pad = pl->pad_bf16;
+  p.sq = st->q;
+  p.sk = st->k;
+  p.sv = st->v;
+  p.so = st->o;
   p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
   p.div_w = make_fastdiv((uint32_t)d.window[2]);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -500,6 +503,6 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
 }  // namespace
 
 int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                      void* stream) {
-  return (int)launch(p, q, k, v, o, static_cast<hipStream_t>(stream));
+                      const swin3d_wattn_strides_t* stride, void* stream) {
+  return (int)launch(p, q, k, v, o, stride, static_cast<hipStream_t>(stream));
 }

@@ -28,8 +28,9 @@ struct Geom {
   int32_t N;         // tokens per window
   float scale;       // f32 kernel: natural-log units
   float bias;
-  float c2;          // bf16 kernel: scale * log2(e)
+  float c2;          // scale * log2(e)
   float bias2;       // cross-region bias * log2(e)
+  int64_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements)
 };
 
 constexpr uint32_t kPadCode = 0xFFu;
@@ -105,7 +106,6 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
   }
   __syncthreads();
 
-  const size_t RS = (size_t)g.heads * DH;
   const size_t hoff = (size_t)head * DH;
   constexpr int C = DH / 4;
   for (int idx = tid; idx < g.N * C; idx += blockDim.x) {
@@ -113,9 +113,8 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
     const int32_t t = tokS[n];
     float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
     if (t >= 0) {
-      const size_t off = (size_t)t * RS + hoff + 4 * c;
-      kk = *reinterpret_cast<const float4*>(k + off);
-      vv = *reinterpret_cast<const float4*>(v + off);
+      kk = *reinterpret_cast<const float4*>(k + (size_t)t * g.sk + hoff + 4 * c);
+      vv = *reinterpret_cast<const float4*>(v + (size_t)t * g.sv + hoff + 4 * c);
     }
     *reinterpret_cast<float4*>(Ks + n * DH + 4 * c) = kk;
     *reinterpret_cast<float4*>(Vs + n * DH + 4 * c) = vv;
@@ -127,7 +126,8 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
   const int32_t t = tokS[n];
   if (t < 0) return;  // padding query: cropped, never written
   const uint32_t cq = codeS[n];
-  const size_t qoff = (size_t)t * RS + hoff;
+  const size_t qoff = (size_t)t * g.sq + hoff;
+  const size_t ooff = (size_t)t * g.so + hoff;
 
   float qr[DH];
 #pragma unroll
@@ -178,12 +178,12 @@ __global__ __launch_bounds__(256) void wattn_f32_kernel(const float* __restrict_
   const float inv = 1.0f / l;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    *reinterpret_cast<float4*>(o + qoff + 4 * c) =
+    *reinterpret_cast<float4*>(o + ooff + 4 * c) =
         make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
   }
 }
 
-Geom make_geom(const swin3d_wattn_plan* p) {
+Geom make_geom(const swin3d_wattn_plan* p, const swin3d_wattn_strides_t* st) {
   Geom g;
   const swin3d_wattn_desc_t& d = p->desc;
   g.X[0] = d.D;
@@ -201,6 +201,10 @@ Geom make_geom(const swin3d_wattn_plan* p) {
   g.bias = d.cross_region_bias;
   g.c2 = p->c2;
   g.bias2 = p->bias2;
+  g.sq = st->q;
+  g.sk = st->k;
+  g.sv = st->v;
+  g.so = st->o;
   return g;
 }
 
@@ -208,7 +212,7 @@ size_t f32_lds_bytes(int N, int dh) { return (size_t)N * dh * 4 * 2 + (size_t)N 
 
 template <int DH>
 hipError_t launch(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                      hipStream_t s) {
+                  const swin3d_wattn_strides_t* st, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
@@ -217,7 +221,7 @@ hipError_t launch(const swin3d_wattn_plan* p, const void* q, const void* k, cons
                                    (int)f32_lds_bytes(256, DH));
   });
   if (attr_err != hipSuccess) return attr_err;
-  Geom g = make_geom(p);
+  Geom g = make_geom(p, st);
   const float* qq = static_cast<const float*>(q);
   const float* kk = static_cast<const float*>(k);
   const float* vv = static_cast<const float*>(v);
@@ -230,8 +234,9 @@ hipError_t launch(const swin3d_wattn_plan* p, const void* q, const void* k, cons
 }  // namespace
 
 int wattn_launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                     void* stream) {
+                     const swin3d_wattn_strides_t* stride, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = p->desc.head_dim == 32 ? launch<32>(p, q, k, v, o, s) : launch<64>(p, q, k, v, o, s);
+  const hipError_t e = p->desc.head_dim == 32 ? launch<32>(p, q, k, v, o, stride, s)
+                                              : launch<64>(p, q, k, v, o, stride, s);
   return (int)e;
 }

@@ -22,8 +22,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = sw.load_library()
     names = _declared_functions()
-    assert names == sorted(["swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_destroy",
-                            "swin3d_wattn_strerror", "swin3d_wattn_get_info"])
+    assert names == sorted(["swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_run_strided",
+                            "swin3d_wattn_destroy", "swin3d_wattn_strerror", "swin3d_wattn_get_info"])
     for n in names:
         assert hasattr(lib, n), n
         assert hasattr(sw, n), n  # the binding uses the same names
@@ -129,6 +129,30 @@ def test_run_rejects_bad_pointers_before_launch():
     assert sw.swin3d_wattn_run(h, 0, k, v, o, 0) == -1       # null
     assert sw.swin3d_wattn_run(h, q, k, v, q + 16, 0) == -1  # o overlaps q
     assert sw.swin3d_wattn_run(h, q, k, v, v - n + 16, 0) == -1  # o overlaps v
+    sw.swin3d_wattn_destroy(h)
+
+
+def test_run_strided_rejects_before_launch():
+    """Strides below heads*head_dim or not a multiple of 16 bytes, null strides and an O span that
+    overlaps Q, K or V are refused on the host."""
+    rc, h = _create(B=1, D=2, H=6, W=12, heads=2)  # bf16, 144 tokens, 128 elements per token
+    assert rc == 0
+    tokens, row = 2 * 6 * 12, 2 * 64
+    S = sw.Swin3dWattnStrides
+    base = 1 << 40
+    fused = S(3 * row, 3 * row, 3 * row, row)
+    q, k, v = base, base + row * 2, base + 2 * row * 2
+    o = base + tokens * 3 * row * 2 + 4096          # just past the fused buffer
+    run = lambda qq, kk, vv, oo, st: sw.swin3d_wattn_run_strided(h, qq, kk, vv, oo, st, 0)
+    assert run(q, k, v, o, S(row - 8, 3 * row, 3 * row, row)) == -1      # stride below a token
+    assert run(q, k, v, o, S(3 * row + 4, 3 * row, 3 * row, row)) == -1  # 8 bytes: not 16-aligned
+    assert run(q, k, v, o, S(3 * row, 3 * row, 3 * row, 0)) == -1
+    assert run(q, k, v, o + 8, fused) == -1                              # misaligned pointer
+    assert sw.load_library().swin3d_wattn_run_strided(h, q, k, v, o, None, 0) == -1
+    span_v = ((tokens - 1) * 3 * row + row) * 2
+    assert run(q, k, v, v + span_v - 16, fused) == -1                    # o starts inside v's span
+    assert run(q, k, v, q - ((tokens - 1) * row + row) * 2 + 16, fused) == -1  # o ends inside q's span
+    assert run(0, k, v, o, fused) == -1
     sw.swin3d_wattn_destroy(h)
 
 

@@ -1,0 +1,74 @@
+"""GPU parity of the strided entry point: Q, K and V read straight out of a fused
+projection buffer [B, D, H, W, 3, heads, head_dim], O written into a wider buffer.
+
+The strided run must give bit-identical results to the contiguous run on the same
+values (only addresses differ), match the fp64 oracle, and leave every element of
+the wide output buffer outside the (token, head, dim) positions untouched."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import swin3d_window_attention_amd as sw
+from _gpu import check, device_inputs, oracle_full, run_gpu, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (name, B, D, H, W, heads, head_dim, shift, dtype, bias)
+    ("stage3_pad", None, None, None, None, None, None, None, None, -100.0),
+    ("tiny_f32", None, None, None, None, None, None, None, None, -math.inf),
+    ("ragged_bf16", 2, 3, 7, 13, 3, 64, (1, 5, 11), "bf16", -math.inf),
+    ("ragged_f32", 1, 4, 44, 30, 2, 32, (1, 3, 6), "f32", -100.0),
+]
+
+
+def _workload(case):
+    name, B, D, H, W, h, dh, shift, dt, _ = case
+    if B is None:
+        return datagen.WORKLOADS[name]
+    return datagen.small_workload(name, B, D, H, W, h, dh, (2, 6, 12), shift, dt, seed=23)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_fused_qkv_and_wide_output(case):
+    wl, bias = _workload(case), case[-1]
+    x = device_inputs(wl)
+    contiguous = run_gpu(wl, bias, x)
+    B, D, H, W, h, dh = wl.shape
+    fused = torch.stack([x["q"], x["k"], x["v"]], dim=4).contiguous()  # [B, D, H, W, 3, h, dh]
+    q, k, v = fused[..., 0, :, :], fused[..., 1, :, :], fused[..., 2, :, :]
+    extra = 64  # elements of padding after each token's row in the output buffer
+    wide = torch.full((B, D, H, W, h * dh + extra), float("nan"), dtype=x["q"].dtype, device="cuda")
+    ibits = torch.int16 if wl.dtype == "bf16" else torch.int32
+    before = wide.view(ibits).clone()
+    o = wide[..., :h * dh].unflatten(-1, (h, dh))
+    assert o.stride()[3] == h * dh + extra and q.stride()[3] == 3 * h * dh
+    say(f"[gpu] strided {wl.name} shape={wl.shape} bias={bias}")
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.dtype, scale=wl.scale,
+                   cross_region_bias=bias)
+    plan.run(q, k, v, o)
+    torch.cuda.synchronize()
+    # same values as the contiguous path, bit for bit
+    assert torch.equal(o.contiguous().view(ibits), contiguous.view(ibits))
+    # the padding after each row is untouched
+    assert torch.equal(wide.view(ibits)[..., h * dh:], before[..., h * dh:])
+    # and the oracle agrees
+    got = to_f64(o.contiguous())
+    heads = [0, h - 1]
+    ref = oracle_full(wl, bias, heads)
+    check(wl, np.stack([got[..., i, :] for i in ref]), np.stack(list(ref.values())), f"strided heads {heads}")
+
+
+def test_binding_rejects_uneven_views():
+    wl = datagen.WORKLOADS["stage3_pad"]
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.dtype, scale=wl.scale)
+    x = torch.zeros(wl.shape, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(x)
+    with pytest.raises(ValueError):  # heads and head_dim swapped in memory
+        plan.run(x.transpose(-1, -2).contiguous().transpose(-1, -2), x, x, o)
+    with pytest.raises(ValueError):  # tokens not evenly spaced: the first 90 W columns of a wider grid
+        wide = torch.zeros((1, 4, 45, 100, 32, 64), dtype=torch.bfloat16, device="cuda")
+        plan.run(wide[:, :, :, :90], x, x, o)
