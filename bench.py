@@ -125,8 +125,9 @@ def main():
     ap.add_argument("--warmup-ms", type=float, default=300.0, help="minimum warm-up time on the GPU")
     ap.add_argument("--bias", type=float, default=-100.0)
     ap.add_argument("--workload", default="stage1",
-                    help="stage1 (default, the headline line) or another bf16 parity workload: "
-                         "stage2, stage2_s0, stage3_pad, stress_hres")
+                    help="stage1 (default, the headline line) or another workload: stage2, stage2_s0, "
+                         "stage3_pad, stress_hres (bf16), stage1_f32_split, stage3_pad_f32_split, "
+                         "stress_f32_split (FP32 I/O on the split-bf16 matrix-core kernel)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
@@ -152,7 +153,7 @@ def main():
     import swin3d_window_attention_amd as sw
 
     wl = datagen.WORKLOADS[args.workload]
-    if wl.dtype != "bf16":
+    if wl.plan_dtype not in ("bf16", "f32_split"):
         sys.exit(f"bench.py: workload {wl.name} is a {wl.dtype} parity case, not a benchmark")
     headline = wl.name == "stage1"
     dev = torch.device("cuda:0")
@@ -160,7 +161,7 @@ def main():
     log(f"[bench] inputs {wl.shape} {wl.dtype}")
     x = {t: datagen.to_torch(datagen.full_io(wl, t), wl.dtype).to(dev) for t in ("q", "k", "v")}
     o = torch.empty_like(x["q"])
-    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.dtype, scale=wl.scale,
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.plan_dtype, scale=wl.scale,
                    cross_region_bias=args.bias)
     info = plan.info()
     stream = torch.cuda.current_stream(dev)
@@ -228,8 +229,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded iid N(0,1) rounded to bf16)",
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32 I/O, bf16x3 split products, f32 softmax",
+        "data": ("synthetic (seeded iid N(0,1) rounded to bf16)" if wl.dtype == "bf16"
+                 else "synthetic (seeded iid float32 draws)"),
         "config": {
             "workload": ("0.25-degree stage-1-like window attention" if headline
                          else f"{wl.name} window attention"),

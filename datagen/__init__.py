@@ -48,6 +48,11 @@ class Workload:
     seed: int
     qk_mult: float = 1.0  # power-of-two multiplier applied to Q and K after rounding
     v_dist: str = "normal"  # "normal" -> N(0,1); "uniform" -> U(-1, 1)
+    plan: str = ""  # library dtype when it differs from the I/O dtype ("f32_split")
+
+    @property
+    def plan_dtype(self) -> str:
+        return self.plan or self.dtype
 
     @property
     def shape(self):
@@ -66,7 +71,7 @@ class Workload:
         return dataclasses.replace(self, shift=tuple(shift), name=name or self.name)
 
 
-# The five workloads. Sizes follow the three ERA5 encoder latent stages of a
+# The workloads. Sizes follow the three ERA5 encoder latent stages of a
 # 0.25-degree grid (721x1440 -> 4 x 180 x 360 tokens at stage 1), one tiny fp32
 # case for exhaustive checks and one high-resolution stress case with large
 # logits (Q, K scaled by 8) and uniform V.
@@ -78,6 +83,14 @@ WORKLOADS = {
     "stage3_pad": Workload("stage3_pad", 1, 4, 45, 90, 32, 64, (2, 6, 12), (1, 3, 6), "bf16", 3),
     "stress_hres": Workload("stress_hres", 2, 4, 450, 900, 8, 64, (2, 6, 12), (1, 3, 6), "bf16", 4,
                             qk_mult=8.0, v_dist="uniform"),
+    # FP32-I/O runs of the stage shapes (unrounded float32 draws) for the split-bf16
+    # matrix-core path and the exact fp32 path
+    "stage1_f32_split": Workload("stage1_f32_split", 1, 4, 180, 360, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 1,
+                                 plan="f32_split"),
+    "stage3_pad_f32_split": Workload("stage3_pad_f32_split", 1, 4, 45, 90, 32, 64, (2, 6, 12), (1, 3, 6),
+                                     "f32", 3, plan="f32_split"),
+    "stress_f32_split": Workload("stress_f32_split", 1, 4, 90, 180, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 4,
+                                 qk_mult=8.0, v_dist="uniform", plan="f32_split"),
 }
 
 
@@ -120,6 +133,8 @@ def slice_io(wl: Workload, tensor: str, b: int, d: int) -> np.ndarray:
     """The (b, d) slice in the I/O dtype: float32 array, or uint16 bf16 bit patterns."""
     x = slice_f32(wl, tensor, b, d)
     if wl.dtype == "f32":
+        if tensor in ("q", "k") and wl.qk_mult != 1.0:
+            x = x * np.float32(wl.qk_mult)  # a power of two: exact
         return x
     bits = f32_to_bf16_bits(x)
     if tensor in ("q", "k") and wl.qk_mult != 1.0:

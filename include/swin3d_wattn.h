@@ -60,8 +60,14 @@ extern "C" {
 #define SWIN3D_WATTN_ELAUNCH (-3)     /* the HIP runtime refused the launch */
 
 typedef enum {
-  SWIN3D_WATTN_F32 = 0,  /* float32 I/O, float32 arithmetic */
-  SWIN3D_WATTN_BF16 = 1  /* bfloat16 I/O, bf16 products, float32 softmax and accumulation */
+  SWIN3D_WATTN_F32 = 0,       /* float32 I/O, float32 arithmetic */
+  SWIN3D_WATTN_BF16 = 1,      /* bfloat16 I/O, bf16 products, float32 softmax and accumulation */
+  SWIN3D_WATTN_F32_SPLIT = 2  /* float32 I/O; Q K^T and P V on the matrix cores from bf16
+                                 hi/lo splits of every operand (three products: hi*hi,
+                                 lo*hi, hi*lo), float32 softmax and accumulation. The
+                                 FP32-fidelity mode at matrix-core speed, in the role of the
+                                 pages' TF32_ACC_FP32 mode (README, "Window attention
+                                 kernels"); products keep ~16 significant bits */
 } swin3d_wattn_dtype_t;
 
 /* Problem description, copied into the plan by swin3d_wattn_create. */
@@ -79,8 +85,9 @@ typedef struct {
 typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 
 /* Validate *desc and build a plan. Host-only: no device is touched.
- * Supported: dtype BF16 with head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with
- * head_dim 32 or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31.
+ * Supported: dtypes BF16 and F32_SPLIT with head_dim 64, wd*wh*ww = 144 and
+ * heads < 65536; dtype F32 with head_dim 32 or 64 and wd*wh*ww <= 256.
+ * B*D*H*W must be < 2^31.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
 int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
@@ -139,7 +146,8 @@ typedef struct {
   int64_t tokens;           /* B*D*H*W real tokens */
   int64_t workgroups;       /* workgroups one run launches */
   int32_t threads_per_workgroup;
-  int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel */
+  int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel,
+                               2 = f32 split-bf16 matrix-core kernel */
 } swin3d_wattn_info_t;
 
 /* Fill *info for a plan. Host-only. Returns 0 or EINVAL. */

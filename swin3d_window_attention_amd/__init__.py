@@ -18,8 +18,9 @@ import threading
 
 __all__ = [
     "SWIN3D_WATTN_OK", "SWIN3D_WATTN_EINVAL", "SWIN3D_WATTN_EUNSUPPORTED", "SWIN3D_WATTN_ELAUNCH",
-    "SWIN3D_WATTN_F32", "SWIN3D_WATTN_BF16", "Swin3dWattnDesc", "Swin3dWattnInfo", "Swin3dWattnError",
-    "lib_path", "load_library", "swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_destroy",
+    "SWIN3D_WATTN_F32", "SWIN3D_WATTN_BF16", "SWIN3D_WATTN_F32_SPLIT", "Swin3dWattnDesc", "Swin3dWattnInfo",
+    "Swin3dWattnStrides", "Swin3dWattnError", "lib_path", "load_library", "swin3d_wattn_create",
+    "swin3d_wattn_run", "swin3d_wattn_run_strided", "swin3d_wattn_destroy",
     "swin3d_wattn_strerror", "swin3d_wattn_get_info", "Plan", "window_attention",
 ]
 
@@ -29,6 +30,7 @@ SWIN3D_WATTN_EUNSUPPORTED = -2
 SWIN3D_WATTN_ELAUNCH = -3
 SWIN3D_WATTN_F32 = 0
 SWIN3D_WATTN_BF16 = 1
+SWIN3D_WATTN_F32_SPLIT = 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libswin3d_wattn.so"
@@ -134,13 +136,22 @@ def swin3d_wattn_get_info(plan):
 # ---- convenience layer --------------------------------------------------
 
 def _dtype_code(dtype) -> int:
+    """Plan dtype code: "f32" (exact FP32 arithmetic), "bf16", or "f32_split" (FP32 I/O with
+    split-bf16 matrix-core products); a torch dtype maps to "f32" or "bf16"."""
     import torch
 
     if dtype in (torch.float32, "f32", "float32"):
         return SWIN3D_WATTN_F32
     if dtype in (torch.bfloat16, "bf16", "bfloat16"):
         return SWIN3D_WATTN_BF16
+    if dtype == "f32_split":
+        return SWIN3D_WATTN_F32_SPLIT
     raise ValueError(f"unsupported dtype {dtype}")
+
+
+def _io_code(code: int) -> int:
+    """The tensor dtype code a plan dtype reads and writes."""
+    return SWIN3D_WATTN_F32 if code == SWIN3D_WATTN_F32_SPLIT else code
 
 
 def make_desc(B, D, H, W, heads, head_dim, window=(2, 6, 12), shift=(0, 0, 0), dtype="bf16",
@@ -210,7 +221,7 @@ class Plan:
                 raise ValueError("q, k, v, o must be device tensors")
             if tuple(t.shape) != self.shape:
                 raise ValueError(f"expected shape {self.shape}, got {tuple(t.shape)}")
-            if _dtype_code(t.dtype) != self.desc.dtype:
+            if _dtype_code(t.dtype) != _io_code(self.desc.dtype):
                 raise ValueError("tensor dtype does not match the plan")
             strides.append(self._token_stride(t))
         if stream is None:
@@ -242,12 +253,13 @@ class Plan:
 
 
 def window_attention(q, k, v, window=(2, 6, 12), shift=(0, 0, 0), scale=None, cross_region_bias=-100.0,
-                     out=None):
-    """Swin3D shifted-window attention of grid-layout device tensors [B, D, H, W, heads, head_dim]."""
+                     out=None, precision=None):
+    """Swin3D shifted-window attention of grid-layout device tensors [B, D, H, W, heads, head_dim].
+    precision: None (the tensors' dtype), or "f32_split" for float32 tensors on the matrix cores."""
     import torch
 
     B, D, H, W, heads, dh = q.shape
-    plan = Plan(B, D, H, W, heads, dh, window, shift, q.dtype, scale, cross_region_bias)
+    plan = Plan(B, D, H, W, heads, dh, window, shift, precision or q.dtype, scale, cross_region_bias)
     if out is None:
         out = torch.empty_like(q)
     plan.run(q, k, v, out)

@@ -62,7 +62,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     if (d.window[a] <= 0) return SWIN3D_WATTN_EINVAL;
     if (d.shift[a] < 0 || d.shift[a] >= d.window[a]) return SWIN3D_WATTN_EINVAL;
   }
-  if (d.dtype != SWIN3D_WATTN_F32 && d.dtype != SWIN3D_WATTN_BF16) return SWIN3D_WATTN_EINVAL;
+  if (d.dtype != SWIN3D_WATTN_F32 && d.dtype != SWIN3D_WATTN_BF16 && d.dtype != SWIN3D_WATTN_F32_SPLIT)
+    return SWIN3D_WATTN_EINVAL;
   if (!std::isfinite(d.scale) || !(d.scale > 0.0f)) return SWIN3D_WATTN_EINVAL;
   if (std::isnan(d.cross_region_bias) || d.cross_region_bias > 0.0f) return SWIN3D_WATTN_EINVAL;
 
@@ -84,9 +85,12 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   const int32_t N = (int32_t)N64;
 
   int32_t kernel = -1, threads = 0;
-  if (d.dtype == SWIN3D_WATTN_BF16) {
+  if (d.dtype == SWIN3D_WATTN_BF16 || d.dtype == SWIN3D_WATTN_F32_SPLIT) {
     // the launch grid is (window, head); its second dimension stays below 2^16
-    if (d.head_dim == 64 && N == 144 && d.heads < 65536) { kernel = 1; threads = 256; }
+    if (d.head_dim == 64 && N == 144 && d.heads < 65536) {
+      kernel = d.dtype == SWIN3D_WATTN_BF16 ? 1 : 2;
+      threads = 256;
+    }
   } else {
     if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
       kernel = 0;
@@ -223,8 +227,9 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
   }
   if (overlaps(o, span[3], q, span[0]) || overlaps(o, span[3], k, span[1]) || overlaps(o, span[3], v, span[2]))
     return SWIN3D_WATTN_EINVAL;
-  const int e = plan->kernel == 1 ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
-                                  : wattn_launch_f32(plan, q, k, v, o, st, stream);
+  const int e = plan->kernel == 1   ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
+                : plan->kernel == 2 ? wattn_launch_f32x3(plan, q, k, v, o, st, stream)
+                                    : wattn_launch_f32(plan, q, k, v, o, st, stream);
   return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }
 

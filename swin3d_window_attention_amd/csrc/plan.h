@@ -14,7 +14,7 @@ struct swin3d_wattn_plan {
   int64_t tokens;           // B * D * H * W
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
-  int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA
+  int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA, 2: f32 split-bf16 MFMA
   int64_t workgroups;       // workgroups one run launches
   int32_t threads;          // threads per workgroup
   float c2;                 // scale * log2(e)
@@ -28,7 +28,8 @@ struct swin3d_wattn_plan {
   int32_t special[3][3];
 };
 
-// Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip).
+// Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip,
+// wattn_f32x3.hip).
 // Each launches its kernel for the plan on `stream` (a hipStream_t) and
 // returns the HIP runtime's status (0 = success). `stride` holds the token
 // strides of Q, K, V and O in elements, already validated.
@@ -36,3 +37,5 @@ int wattn_launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, c
                      const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                       const swin3d_wattn_strides_t* stride, void* stream);
+int wattn_launch_f32x3(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                       const swin3d_wattn_strides_t* stride, void* stream);

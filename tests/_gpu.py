@@ -11,10 +11,7 @@ import datagen
 import oracle
 import swin3d_window_attention_amd as sw
 
-# Acceptance bars against the fp64 oracle, over real tokens.
-F32_MAX_ABS = 1e-5
-BF16_MAX_ABS = 1e-2
-BF16_REL_L2 = 5e-3
+from _tolerances import BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, SPLIT_TOL  # noqa: F401
 
 
 def say(msg: str) -> None:
@@ -36,7 +33,7 @@ def io_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 
 def run_gpu(wl: datagen.Workload, bias: float, x: dict, fill=float("nan")) -> torch.Tensor:
     say(f"[gpu] run {wl.name} shape={wl.shape} shift={wl.shift} bias={bias}")
-    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.dtype, scale=wl.scale,
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.plan_dtype, scale=wl.scale,
                    cross_region_bias=bias)
     o = torch.full_like(x["q"], fill)
     plan.run(x["q"], x["k"], x["v"], o)
@@ -59,7 +56,11 @@ def check(wl: datagen.Workload, got: np.ndarray, ref: np.ndarray, what: str = ""
     assert np.all(np.isfinite(got)), f"{wl.name} {what}: non-finite output"
     max_abs, rel = errors(got, ref)
     say(f"[gpu] {wl.name} {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
-    if wl.dtype == "f32":
+    if wl.plan_dtype == "f32_split":
+        tol_abs, tol_rel = SPLIT_TOL[wl.qk_mult]
+        assert max_abs <= tol_abs, (wl.name, what, max_abs)
+        assert rel <= tol_rel, (wl.name, what, rel)
+    elif wl.dtype == "f32":
         assert max_abs <= F32_MAX_ABS, (wl.name, what, max_abs)
     else:
         assert max_abs <= BF16_MAX_ABS, (wl.name, what, max_abs)

@@ -97,6 +97,20 @@ def test_create_rejects(kw, code):
     assert rc == code and h is None
 
 
+def test_f32_split_plans():
+    """FP32 I/O on the matrix cores: head_dim 64 and 144-slot windows only; kernel 2."""
+    rc, h = _create(dtype=2)
+    assert rc == 0
+    rc2, info = sw.swin3d_wattn_get_info(h)
+    assert rc2 == 0 and info.kernel == 2 and info.threads_per_workgroup == 256
+    sw.swin3d_wattn_destroy(h)
+    for kw in (dict(dtype=2, head_dim=32), dict(dtype=2, window=(2, 6, 6), shift=(1, 3, 3)),
+               dict(dtype=2, D=1, H=1, W=1, heads=65536)):
+        rc, h = _create(**kw)
+        assert rc == -2 and h is None, kw
+    assert sw.make_desc(1, 2, 6, 12, 1, 64, dtype="f32_split").dtype == sw.SWIN3D_WATTN_F32_SPLIT == 2
+
+
 def test_create_accepts_edge_cases():
     for kw in [dict(cross_region_bias=-math.inf), dict(shift=(0, 0, 0)), dict(shift=(1, 5, 11)),
                dict(D=1, H=1, W=1), dict(D=1, H=1, W=1, heads=65535), dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)),

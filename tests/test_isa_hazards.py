@@ -130,3 +130,72 @@ def test_bf16_kernel_occupancy(asm):
     """Four workgroups of the matrix-core kernel share a CU (four waves per SIMD)."""
     m = re.search(r"wattn_bf16_item\w*:.*?; Occupancy: (\d+)", asm, re.S)
     assert m and int(m.group(1)) >= 4
+
+
+def _reg_range(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return int(m.group(1)), int(m.group(2))
+    m = re.match(r"v(\d+)$", tok)
+    return (int(m.group(1)), int(m.group(1))) if m else None
+
+
+def _kernels_with_labels(asm_text):
+    """Map kernel symbol -> instruction lines, with '<label>' marking basic-block starts."""
+    out, cur = {}, None
+    for line in asm_text.splitlines():
+        s = line.strip()
+        m = re.match(r"^(_Z\S+):\s*(;.*)?$", s)
+        if m:
+            cur = m.group(1)
+            out[cur] = []
+            continue
+        if cur is None or not s or s.startswith(";") or (s.startswith(".") and not s.endswith(":")):
+            continue
+        out[cur].append("<label>" if s.endswith(":") else s)
+        if s.startswith("s_endpgm"):
+            cur = None
+    return out
+
+
+def dead_load_words(instrs):
+    """16-byte global loads one of whose destination words is overwritten, inside the same basic
+    block, before anything reads it. That is either wasted bandwidth or a miscompile: the compiler
+    once built a bf16 split element by element and took every element from word 0 of the load."""
+    hits = []
+    for i, line in enumerate(instrs):
+        m = re.match(r"global_load_dwordx4 v\[(\d+):(\d+)\]", line)
+        if not m:
+            continue
+        for r in range(int(m.group(1)), int(m.group(2)) + 1):
+            for later in instrs[i + 1:]:
+                if later == "<label>" or later.startswith(("s_cbranch", "s_branch", "s_setpc")):
+                    break
+                parts = re.split(r"[\s,]+", later)
+                srcs = [_reg_range(p) for p in parts[2:]]
+                if any(s and s[0] <= r <= s[1] for s in srcs) or parts[0].startswith(("ds_write", "global_store")) \
+                        and any(s and s[0] <= r <= s[1] for s in [_reg_range(p) for p in parts[1:]]):
+                    break
+                dst = _reg_range(parts[1]) if len(parts) > 1 else None
+                if dst and dst[0] <= r <= dst[1] and not parts[0].startswith(("s_", "ds_write", "global_store")):
+                    hits.append((i, r, line, later))
+                    break
+    return hits
+
+
+def test_every_loaded_word_is_used(asm):
+    kernels = _kernels_with_labels(asm)
+    for name, instrs in kernels.items():
+        hits = dead_load_words(instrs)
+        assert not hits, f"{name}: {len(hits)} loaded words overwritten unread, first: {hits[0]}"
+
+
+def test_dead_word_scanner_flags_the_pattern():
+    bad = ["global_load_dwordx4 v[0:3], v6, s[0:1] nt",
+           "v_cvt_pk_bf16_f32 v1, v0, s0",
+           "global_store_dwordx4 v6, v[1:4], s[2:3]"]
+    assert dead_load_words(bad)
+    ok = ["global_load_dwordx4 v[0:3], v6, s[0:1] nt",
+          "ds_write_b128 v7, v[0:3]",
+          "v_mov_b32_e32 v1, 0"]
+    assert not dead_load_words(ok)
