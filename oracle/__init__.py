@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for Swin3D shifted-window attention (test infrastructure only).
+"""fp64 CPU oracle for Swin3D shifted-window attention and the fused AdaLN +
+residual step (test infrastructure only).
 
 Only the tests, the build entry point's smoke check and the benchmark's CPU
 baseline may import this package; the GPU library never does.
@@ -17,3 +18,4 @@ from .swin3d import (  # noqa: F401
     window_slot_coords,
     windows_attention,
 )
+from .adaln import adaln_residual, layer_norm  # noqa: F401

@@ -1,0 +1,85 @@
+"""Pins of the AdaLN + residual oracle against things it does not compute itself."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_layer_norm_matches_torch_layer_norm():
+    """A library routine: torch.nn.functional.layer_norm in float64 on the CPU (no affine)."""
+    x = _rand((3, 17, 256), 0) * 3.0 + 1.5
+    for eps in (1e-5, 1e-2):
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (256,), eps=eps).numpy()
+        assert np.allclose(oracle.layer_norm(x, eps), ref, rtol=0, atol=1e-12)
+
+
+def test_normalised_rows_have_zero_mean_and_the_closed_form_variance():
+    x = _rand((4, 9, 512), 1) * 2.0 - 0.7
+    eps = 1e-3
+    xh = oracle.layer_norm(x, eps)
+    var = x.var(axis=-1)
+    assert np.allclose(xh.mean(axis=-1), 0.0, atol=1e-13)
+    assert np.allclose(xh.var(axis=-1), var / (var + eps), rtol=1e-12)
+
+
+def test_biased_variance_closed_form():
+    """Row (1, -1, 1, -1, ...): mean 0, biased variance exactly 1, so xhat = x / sqrt(1 + eps)
+    (an unbiased variance, C / (C - 1), would give a different value)."""
+    C, eps = 256, 1e-5
+    x = np.tile([1.0, -1.0], C // 2)[None, None]
+    xh = oracle.layer_norm(x, eps)
+    assert np.allclose(xh, x / np.sqrt(1.0 + eps), rtol=1e-15)
+
+
+def test_constant_rows_give_residual_plus_beta():
+    x = np.full((2, 5, 256), 3.25)
+    res, beta = _rand((2, 5, 256), 2), _rand((2, 256), 3)
+    out = oracle.adaln_residual(x, res, _rand((2, 256), 4), beta, 1e-5)
+    assert np.array_equal(out, res + beta[:, None, :])
+
+
+def test_shift_and_scale_invariance():
+    x = _rand((2, 7, 512), 5)
+    xh = oracle.layer_norm(x, 1e-12)
+    assert np.allclose(oracle.layer_norm(3.5 * x - 11.0, 1e-12 * 3.5 ** 2), xh, atol=1e-9)
+
+
+def test_film_and_residual_terms():
+    """out - res - beta is gamma times the normalised row: linear in gamma, per batch element."""
+    B, T, C, eps = 2, 6, 256, 1e-5
+    x, res = _rand((B, T, C), 6), _rand((B, T, C), 7)
+    g, b = _rand((B, C), 8), _rand((B, C), 9)
+    out = oracle.adaln_residual(x, res, g, b, eps)
+    xh = oracle.layer_norm(x, eps)
+    for bi in range(B):
+        assert np.allclose(out[bi] - res[bi] - b[bi], g[bi] * xh[bi], atol=1e-13)
+    # gamma = 1, beta = 0, res = 0 reduces to the library LayerNorm
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (C,), eps=eps).numpy()
+    assert np.allclose(oracle.adaln_residual(x, np.zeros_like(x), np.ones((B, C)), np.zeros((B, C)), eps),
+                       ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("mutation", ["unbiased", "eps_outside", "no_center", "beta_before_gamma"])
+def test_mutations_are_caught(mutation):
+    """Plausible mistakes in a LayerNorm/FiLM oracle fail the closed forms above."""
+    def bad_ln(x, eps):
+        mean = x.mean(axis=-1, keepdims=True)
+        if mutation == "unbiased":
+            return (x - mean) / np.sqrt(x.var(axis=-1, ddof=1, keepdims=True) + eps)
+        if mutation == "eps_outside":
+            return (x - mean) / (np.sqrt(x.var(axis=-1, keepdims=True)) + eps)
+        if mutation == "no_center":
+            return x / np.sqrt(x.var(axis=-1, keepdims=True) + eps)
+        return (x - mean) / np.sqrt(x.var(axis=-1, keepdims=True) + eps)
+    C, eps = 256, 0.25
+    x = np.tile([1.0, -1.0], C // 2)[None, None] + (0.5 if mutation == "no_center" else 0.0)
+    expect = (x - x.mean()) / np.sqrt(1.0 + eps)
+    g, b = np.full((1, C), 2.0), np.full((1, C), 0.5)
+    got = bad_ln(x, eps)
+    out = got * g[:, None] + b[:, None] if mutation != "beta_before_gamma" else (got + b[:, None]) * g[:, None]
+    assert not np.allclose(out, expect * g[:, None] + b[:, None], atol=1e-9)
