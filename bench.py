@@ -117,6 +117,56 @@ def copy_calibration(nbytes: int, steps: int):
                       "gbs_read_plus_write": 2 * n * 2 / dt / 1e9}), flush=True)
 
 
+def bench_adaln(args):
+    """The fused AdaLN + residual step at the stage-1 token count (one JSON line)."""
+    import torch
+
+    import datagen
+    import swin3d_window_attention_amd as sw
+
+    wl = datagen.ADALN_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a = datagen.adaln_inputs(wl)
+    x = datagen.to_torch(a["x"], wl.x_dtype).to(dev)
+    res = datagen.to_torch(a["res"], wl.res_dtype).to(dev)
+    g, b = (torch.from_numpy(a[k]).to(dev) for k in ("gamma", "beta"))
+    out_dtype = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    out = torch.empty(wl.shape, dtype=out_dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        sw.adaln_residual(x, res, g, b, wl.eps, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
+        for _ in range(20):
+            sw.adaln_residual(x, res, g, b, wl.eps, out=out)
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        sw.adaln_residual(x, res, g, b, wl.eps, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] adaln {ms * 1000:.1f} us per step")
+    elt = {"bf16": 2, "f32": 4}
+    n = wl.B * wl.rows * wl.C
+    nbytes = n * (elt[wl.x_dtype] + elt[wl.res_dtype] + elt[wl.out_dtype]) + 2 * wl.B * wl.C * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "fused AdaLN + residual tokens/s at the 0.25-degree stage-1 token count",
+        "value": wl.B * wl.rows / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"x {wl.x_dtype}, residual {wl.res_dtype}, out {wl.out_dtype}, f32 math",
+        "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "B": wl.B, "rows": wl.rows, "C": wl.C, "eps": wl.eps},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "algorithmic_bytes_per_launch": nbytes, "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,7 +177,8 @@ def main():
     ap.add_argument("--workload", default="stage1",
                     help="stage1 (default, the headline line) or another workload: stage2, stage2_s0, "
                          "stage3_pad, stress_hres (bf16), stage1_f32_split, stage3_pad_f32_split, "
-                         "stress_f32_split (FP32 I/O on the split-bf16 matrix-core kernel)")
+                         "stress_f32_split (FP32 I/O on the split-bf16 matrix-core kernel), "
+                         "adaln_stage1 (the fused AdaLN + residual step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
@@ -145,6 +196,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.workload.startswith("adaln"):
+        bench_adaln(args)
         return
 
     import torch

@@ -193,3 +193,55 @@ def to_torch(x: np.ndarray, dtype: str):
 def small_workload(name, B, D, H, W, heads, head_dim, window, shift, dtype, seed, **kw) -> Workload:
     """Ad-hoc workload for tests (same generation recipe)."""
     return Workload(name, B, D, H, W, heads, head_dim, tuple(window), tuple(shift), dtype, seed, **kw)
+
+
+# ---- fused AdaLN + residual inputs ------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class AdalnWorkload:
+    """x, res: [B, rows, C] in their I/O dtypes; gamma, beta: [B, C] float32."""
+    name: str
+    B: int
+    rows: int
+    C: int
+    x_dtype: str
+    res_dtype: str
+    out_dtype: str
+    seed: int
+    eps: float = 1e-5
+
+    @property
+    def shape(self):
+        return (self.B, self.rows, self.C)
+
+
+# The stage-1 token count and a 512-channel embedding (8 heads x 64): x is the
+# bf16 output of the attention block's projection, the residual stream and the
+# output stay in float32 between blocks.
+ADALN_WORKLOADS = {
+    "adaln_stage1": AdalnWorkload("adaln_stage1", 1, 4 * 180 * 360, 512, "bf16", "f32", "f32", 21),
+}
+
+
+def adaln_inputs(wl: AdalnWorkload) -> dict:
+    """Seeded inputs in I/O representation (float32 arrays or uint16 bf16 bits). Each row of x has
+    its own offset U(-1, 1) and spread U(0.5, 2) so that centering and scaling both matter;
+    res ~ N(0, 1); gamma = 1 + 0.2 N(0, 1), beta = 0.2 N(0, 1)."""
+    out = {"x": [], "res": [], "gamma": [], "beta": []}
+    for b in range(wl.B):
+        rng = np.random.default_rng([wl.seed, 10, b])
+        mu = rng.uniform(-1.0, 1.0, size=(wl.rows, 1)).astype(np.float32)
+        sd = rng.uniform(0.5, 2.0, size=(wl.rows, 1)).astype(np.float32)
+        x = mu + sd * rng.standard_normal((wl.rows, wl.C), dtype=np.float32)
+        res = np.random.default_rng([wl.seed, 11, b]).standard_normal((wl.rows, wl.C), dtype=np.float32)
+        prng = np.random.default_rng([wl.seed, 12, b])
+        out["gamma"].append(1.0 + 0.2 * prng.standard_normal(wl.C, dtype=np.float32))
+        out["beta"].append(0.2 * prng.standard_normal(wl.C, dtype=np.float32))
+        out["x"].append(f32_to_bf16_bits(x) if wl.x_dtype == "bf16" else x)
+        out["res"].append(f32_to_bf16_bits(res) if wl.res_dtype == "bf16" else res)
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+def io_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """I/O representation -> the float64 values it holds."""
+    return (bf16_bits_to_f32(a) if dtype == "bf16" else a).astype(np.float64)

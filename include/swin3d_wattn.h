@@ -130,6 +130,37 @@ typedef struct {
 int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, const void* k, const void* v, void* o,
                              const swin3d_wattn_strides_t* strides, void* stream);
 
+/* ---- Fused AdaLN + residual ------------------------------------------------
+ * The step the pages fuse around each Swin3D attention block (Flash-Aurora
+ * README, "Kernel fusion for backbone memory traffic": LayerNorm, FiLM
+ * modulation and the residual add without a full-width intermediate, with
+ * FP32 activations between blocks when wanted). For row t of batch element b,
+ * with C channels per row, in FP32:
+ *   xhat = (x - mean) / sqrt(var + eps)      mean, biased variance over C
+ *   out  = res + gamma[b] * xhat + beta[b]
+ */
+typedef struct {
+  int64_t rows;      /* rows (tokens) per batch element */
+  int32_t B;         /* batch elements; gamma and beta hold one row of C per element */
+  int32_t C;         /* channels per row: a multiple of 256, at most 4096 */
+  int32_t x_dtype;   /* SWIN3D_WATTN_F32 or SWIN3D_WATTN_BF16 */
+  int32_t res_dtype; /* likewise */
+  int32_t out_dtype; /* likewise; F32 keeps the residual stream in FP32 between blocks */
+  float eps;         /* > 0 and finite */
+} swin3d_adaln_desc_t;
+
+/* out = res + gamma * LayerNorm(x) + beta on `stream` (a hipStream_t).
+ * x, res, out: device pointers to B*rows*C elements ([B, rows, C] row-major)
+ * of their dtypes; gamma, beta: device pointers to B*C floats ([B, C]); all
+ * 16-byte aligned. out may be res itself when both have the same dtype (the
+ * residual stream updated in place) but must not otherwise overlap x, res,
+ * gamma or beta. B*rows must be < 2^31. Asynchronous; the caller owns every
+ * buffer. Returns 0, EINVAL (null, misaligned, unknown dtype, a size <= 0,
+ * eps not positive and finite, overlap), EUNSUPPORTED (C not a multiple of
+ * 256 or above 4096, B*rows too large) or ELAUNCH. */
+int swin3d_adaln_residual(const swin3d_adaln_desc_t* desc, const void* x, const void* res,
+                          const float* gamma, const float* beta, void* out, void* stream);
+
 /* Release a plan. NULL is a no-op. Returns 0. */
 int swin3d_wattn_destroy(swin3d_wattn_t plan);
 

@@ -22,6 +22,7 @@ __all__ = [
     "Swin3dWattnStrides", "Swin3dWattnError", "lib_path", "load_library", "swin3d_wattn_create",
     "swin3d_wattn_run", "swin3d_wattn_run_strided", "swin3d_wattn_destroy",
     "swin3d_wattn_strerror", "swin3d_wattn_get_info", "Plan", "window_attention",
+    "Swin3dAdalnDesc", "swin3d_adaln_residual", "adaln_residual",
 ]
 
 SWIN3D_WATTN_OK = 0
@@ -58,6 +59,13 @@ class Swin3dWattnInfo(ctypes.Structure):
 class Swin3dWattnStrides(ctypes.Structure):
     """Token strides (elements) of Q, K, V, O: swin3d_wattn_strides_t."""
     _fields_ = [("q", ctypes.c_int64), ("k", ctypes.c_int64), ("v", ctypes.c_int64), ("o", ctypes.c_int64)]
+
+
+class Swin3dAdalnDesc(ctypes.Structure):
+    """swin3d_adaln_desc_t: fused AdaLN + residual over [B, rows, C]."""
+    _fields_ = [("rows", ctypes.c_int64), ("B", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("res_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
 
 
 class Swin3dWattnError(RuntimeError):
@@ -97,6 +105,8 @@ def load_library():
         lib.swin3d_wattn_strerror.restype = ctypes.c_char_p
         lib.swin3d_wattn_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(Swin3dWattnInfo)]
         lib.swin3d_wattn_get_info.restype = ctypes.c_int
+        lib.swin3d_adaln_residual.argtypes = [ctypes.POINTER(Swin3dAdalnDesc)] + [ctypes.c_void_p] * 6
+        lib.swin3d_adaln_residual.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -117,6 +127,11 @@ def swin3d_wattn_run(plan, q: int, k: int, v: int, o: int, stream: int = 0) -> i
 def swin3d_wattn_run_strided(plan, q: int, k: int, v: int, o: int, strides: Swin3dWattnStrides,
                              stream: int = 0) -> int:
     return load_library().swin3d_wattn_run_strided(plan, q, k, v, o, ctypes.byref(strides), stream)
+
+
+def swin3d_adaln_residual(desc: Swin3dAdalnDesc, x: int, res: int, gamma: int, beta: int, out: int,
+                          stream: int = 0) -> int:
+    return load_library().swin3d_adaln_residual(ctypes.byref(desc), x, res, gamma, beta, out, stream)
 
 
 def swin3d_wattn_destroy(plan) -> int:
@@ -263,4 +278,34 @@ def window_attention(q, k, v, window=(2, 6, 12), shift=(0, 0, 0), scale=None, cr
     if out is None:
         out = torch.empty_like(q)
     plan.run(q, k, v, out)
+    return out
+
+
+def adaln_residual(x, res, gamma, beta, eps=1e-5, out=None, out_dtype=None, stream=None):
+    """out = res + gamma[b] * LayerNorm(x) + beta[b] for device tensors x, res [B, rows, C]
+    (bf16 or float32, contiguous) and gamma, beta [B, C] float32. out defaults to a new tensor of
+    out_dtype (default: res's dtype); out may be res itself (in-place residual update)."""
+    import torch
+
+    if x.dim() != 3 or res.shape != x.shape or gamma.shape != (x.shape[0], x.shape[2]) or beta.shape != gamma.shape:
+        raise ValueError("x, res: [B, rows, C]; gamma, beta: [B, C]")
+    for t in (x, res, gamma, beta):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("gamma and beta must be float32")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or res.dtype, device=x.device)
+    if out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, rows, C] tensor")
+    d = Swin3dAdalnDesc(x.shape[1], x.shape[0], x.shape[2], _dtype_code(x.dtype), _dtype_code(res.dtype),
+                        _dtype_code(out.dtype), eps)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = swin3d_adaln_residual(d, x.data_ptr(), res.data_ptr(), gamma.data_ptr(), beta.data_ptr(),
+                               out.data_ptr(), stream)
+    if rc != SWIN3D_WATTN_OK:
+        raise Swin3dWattnError(rc, "swin3d_adaln_residual")
     return out

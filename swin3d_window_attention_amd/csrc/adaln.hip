@@ -1,0 +1,163 @@
+// Fused AdaLN + residual for gfx950 (MI355X): the step around each Swin3D
+// attention block that the Flash-Aurora README fuses ("Kernel fusion for
+// backbone memory traffic": LayerNorm, FiLM modulation and the residual add
+// without a full-width intermediate, optionally emitting FP32 activations
+// between blocks).
+//
+// For token row t of batch element b (C channels):
+//   xhat = (x - mean) / sqrt(var + eps)      (biased variance over C)
+//   out  = res + gamma[b] * xhat + beta[b]
+// x, res and out are each bf16 or fp32; gamma, beta are fp32 [B, C]. All
+// arithmetic is FP32.
+//
+// One wave per row: the row stays in registers (two passes over registers,
+// not over memory), so the kernel reads x and res once and writes out once.
+// Lane l handles the 4-channel units l, l + 64, ..., so every load and store
+// instruction of a wave covers a contiguous span of the row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace {
+
+typedef float floatx4 __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(8)));
+typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+
+constexpr int kWaves = 4;
+constexpr int kMaxUnits = 16;  // C <= 64 lanes x 16 units x 4 channels = 4096
+
+struct FastDiv {
+  uint32_t mul, shr;
+};
+
+// floor(n / d) for 0 <= n < 2^31 (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint32_t shr = 31 + l;
+  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
+}
+
+struct AdalnParams {
+  int32_t rows;   // B * T
+  int32_t C;
+  int32_t units;  // C / 256: 4-channel units per lane
+  FastDiv div_t;  // by T (rows per batch element)
+  float eps;
+  float inv_c;
+};
+
+// 4 channels in, as fp32 (non-temporal: x and res are read once)
+__device__ __forceinline__ floatx4 load4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+}
+__device__ __forceinline__ floatx4 load4(const __bf16* p) {
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return __builtin_convertvector(__builtin_bit_cast(bf16x4_t, w), floatx4);
+}
+// 4 channels out (bf16: round to nearest even, whole-vector conversion)
+__device__ __forceinline__ void store4(float* p, floatx4 v) { *reinterpret_cast<floatx4*>(p) = v; }
+__device__ __forceinline__ void store4(__bf16* p, floatx4 v) {
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4_t));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <typename XT, typename RT, typename OT>
+__global__ __launch_bounds__(64 * kWaves) void adaln_residual_kernel(const XT* __restrict__ x, const RT* res,
+                                                                      const float* __restrict__ gamma,
+                                                                      const float* __restrict__ beta, OT* out,
+                                                                      const AdalnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= p.rows) return;  // whole waves only
+  const int b = (int)fdiv((uint32_t)row, p.div_t);
+  const size_t base = (size_t)row * p.C;
+
+  floatx4 v[kMaxUnits];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxUnits; ++i) {
+    if (i < p.units) {
+      v[i] = load4(x + base + 4 * (lane + 64 * i));
+      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+  }
+  const float mean = wave_sum(s) * p.inv_c;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxUnits; ++i) {
+    if (i < p.units) {
+      const floatx4 d = v[i] - mean;
+      v[i] = d;
+      q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * p.inv_c + p.eps);
+
+  const float* g = gamma + (size_t)b * p.C;
+  const float* be = beta + (size_t)b * p.C;
+#pragma unroll
+  for (int i = 0; i < kMaxUnits; ++i) {
+    if (i < p.units) {
+      const int c = 4 * (lane + 64 * i);
+      const floatx4 gg = *reinterpret_cast<const floatx4*>(g + c);
+      const floatx4 bb = *reinterpret_cast<const floatx4*>(be + c);
+      const floatx4 r = load4(res + base + c);
+      store4(out + base + c, r + gg * (v[i] * rstd) + bb);
+    }
+  }
+}
+
+template <typename XT, typename RT, typename OT>
+hipError_t launch_t(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                    const float* beta, void* out, hipStream_t s) {
+  AdalnParams p;
+  p.rows = (int32_t)(d->rows * d->B);
+  p.C = d->C;
+  p.units = d->C / 256;
+  p.div_t = make_fastdiv((uint32_t)d->rows);
+  p.eps = d->eps;
+  p.inv_c = 1.0f / (float)d->C;
+  const XT* xx = static_cast<const XT*>(x);
+  const RT* rr = static_cast<const RT*>(res);
+  OT* oo = static_cast<OT*>(out);
+  void* args[] = {&xx, &rr, &gamma, &beta, &oo, &p};
+  const unsigned blocks = (unsigned)((p.rows + kWaves - 1) / kWaves);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&adaln_residual_kernel<XT, RT, OT>), dim3(blocks),
+                         dim3(64 * kWaves), args, 0, s);
+}
+
+template <typename XT, typename RT>
+hipError_t launch_o(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                    const float* beta, void* out, hipStream_t s) {
+  return d->out_dtype == SWIN3D_WATTN_BF16 ? launch_t<XT, RT, __bf16>(d, x, res, gamma, beta, out, s)
+                                           : launch_t<XT, RT, float>(d, x, res, gamma, beta, out, s);
+}
+
+template <typename XT>
+hipError_t launch_r(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                    const float* beta, void* out, hipStream_t s) {
+  return d->res_dtype == SWIN3D_WATTN_BF16 ? launch_o<XT, __bf16>(d, x, res, gamma, beta, out, s)
+                                           : launch_o<XT, float>(d, x, res, gamma, beta, out, s);
+}
+
+}  // namespace
+
+int adaln_launch(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                 const float* beta, void* out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = d->x_dtype == SWIN3D_WATTN_BF16 ? launch_r<__bf16>(d, x, res, gamma, beta, out, s)
+                                                       : launch_r<float>(d, x, res, gamma, beta, out, s);
+  return (int)e;
+}

@@ -240,3 +240,25 @@ extern "C" int swin3d_wattn_run(swin3d_wattn_t plan, const void* q, const void* 
   const swin3d_wattn_strides_t st = {row, row, row, row};
   return swin3d_wattn_run_strided(plan, q, k, v, o, &st, stream);
 }
+
+extern "C" int swin3d_adaln_residual(const swin3d_adaln_desc_t* d, const void* x, const void* res,
+                                     const float* gamma, const float* beta, void* out, void* stream) {
+  if (!d || !x || !res || !gamma || !beta || !out) return SWIN3D_WATTN_EINVAL;
+  if (misaligned(x) || misaligned(res) || misaligned(gamma) || misaligned(beta) || misaligned(out))
+    return SWIN3D_WATTN_EINVAL;
+  auto known = [](int32_t t) { return t == SWIN3D_WATTN_F32 || t == SWIN3D_WATTN_BF16; };
+  if (!known(d->x_dtype) || !known(d->res_dtype) || !known(d->out_dtype)) return SWIN3D_WATTN_EINVAL;
+  if (d->rows <= 0 || d->B <= 0 || d->C <= 0) return SWIN3D_WATTN_EINVAL;
+  if (!std::isfinite(d->eps) || !(d->eps > 0.0f)) return SWIN3D_WATTN_EINVAL;
+  if (d->C % 256 != 0 || d->C > 4096) return SWIN3D_WATTN_EUNSUPPORTED;
+  if (d->rows * (int64_t)d->B >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+  const int64_t n = d->rows * d->B * d->C;
+  auto bytes = [n](int32_t t) { return n * (t == SWIN3D_WATTN_BF16 ? 2 : 4); };
+  const int64_t xb = bytes(d->x_dtype), rb = bytes(d->res_dtype), ob = bytes(d->out_dtype);
+  const int64_t pb = (int64_t)d->B * d->C * 4;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, gamma, pb) || overlaps(out, ob, beta, pb))
+    return SWIN3D_WATTN_EINVAL;
+  const bool in_place = out == res && d->out_dtype == d->res_dtype;
+  if (!in_place && overlaps(out, ob, res, rb)) return SWIN3D_WATTN_EINVAL;
+  return adaln_launch(d, x, res, gamma, beta, out, stream) == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
+}

@@ -39,3 +39,6 @@ int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, 
                       const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_f32x3(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                        const swin3d_wattn_strides_t* stride, void* stream);
+// adaln.hip: the fused AdaLN + residual kernel for an already validated desc.
+int adaln_launch(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                 const float* beta, void* out, void* stream);

@@ -16,14 +16,15 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(swin3d_wattn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(swin3d_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = sw.load_library()
     names = _declared_functions()
     assert names == sorted(["swin3d_wattn_create", "swin3d_wattn_run", "swin3d_wattn_run_strided",
-                            "swin3d_wattn_destroy", "swin3d_wattn_strerror", "swin3d_wattn_get_info"])
+                            "swin3d_wattn_destroy", "swin3d_wattn_strerror", "swin3d_wattn_get_info",
+                            "swin3d_adaln_residual"])
     for n in names:
         assert hasattr(lib, n), n
         assert hasattr(sw, n), n  # the binding uses the same names
@@ -175,3 +176,28 @@ def test_strerror():
     for c in (-1, -2, -3):
         assert sw.swin3d_wattn_strerror(c) and sw.swin3d_wattn_strerror(c) != "success"
     assert "unknown" in sw.swin3d_wattn_strerror(42)
+
+
+def test_adaln_rejects_before_launch():
+    """Bad descriptors, null or misaligned pointers and overlaps are refused on the host."""
+    D = sw.Swin3dAdalnDesc
+    base = 1 << 40
+    n = 2 * 100 * 512
+    x, res, out = base, base + 4 * n + 4096, base + 8 * n + 8192   # f32 spans of 4n bytes
+    g, b = base + 16 * n, base + 16 * n + 8192
+    ok = D(100, 2, 512, 1, 0, 0, 1e-5)
+    run = lambda d, *p: sw.swin3d_adaln_residual(d, *p, 0)
+    assert run(D(100, 2, 300, 1, 0, 0, 1e-5), x, res, g, b, out) == -2    # C not a multiple of 256
+    assert run(D(100, 2, 8192, 1, 0, 0, 1e-5), x, res, g, b, out) == -2   # C above 4096
+    assert run(D(100, 2, 512, 1, 0, 0, 0.0), x, res, g, b, out) == -1     # eps
+    assert run(D(100, 2, 512, 1, 0, 0, float("nan")), x, res, g, b, out) == -1
+    assert run(D(0, 2, 512, 1, 0, 0, 1e-5), x, res, g, b, out) == -1
+    assert run(D(100, 2, 512, 2, 0, 0, 1e-5), x, res, g, b, out) == -1    # no split dtype here
+    assert run(D(1 << 30, 4, 256, 1, 0, 0, 1e-5), x, res, g, b, out) == -2  # too many rows
+    assert run(ok, 0, res, g, b, out) == -1
+    assert run(ok, x + 8, res, g, b, out) == -1                            # misaligned
+    assert run(ok, x, res, g, b, x + 16) == -1                             # out overlaps x
+    assert run(ok, x, res, g, b, res + 16) == -1                           # partial overlap with res
+    assert run(D(100, 2, 512, 1, 0, 1, 1e-5), x, res, g, b, res) == -1     # in place needs the same dtype
+    assert run(ok, x, res, g, b, g) == -1                                  # out overlaps gamma
+    assert sw.load_library().swin3d_adaln_residual(None, x, res, g, b, out, 0) == -1

@@ -172,7 +172,9 @@ def dead_load_words(instrs):
                 if later == "<label>" or later.startswith(("s_cbranch", "s_branch", "s_setpc")):
                     break
                 parts = re.split(r"[\s,]+", later)
-                srcs = [_reg_range(p) for p in parts[2:]]
+                # multiply-accumulate forms (v_fmac, v_mac, ...) read their destination too
+                first_src = 1 if "mac" in parts[0] else 2
+                srcs = [_reg_range(p) for p in parts[first_src:]]
                 if any(s and s[0] <= r <= s[1] for s in srcs) or parts[0].startswith(("ds_write", "global_store")) \
                         and any(s and s[0] <= r <= s[1] for s in [_reg_range(p) for p in parts[1:]]):
                     break
