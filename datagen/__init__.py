@@ -83,6 +83,9 @@ WORKLOADS = {
     "stage3_pad": Workload("stage3_pad", 1, 4, 45, 90, 32, 64, (2, 6, 12), (1, 3, 6), "bf16", 3),
     "stress_hres": Workload("stress_hres", 2, 4, 450, 900, 8, 64, (2, 6, 12), (1, 3, 6), "bf16", 4,
                             qk_mult=8.0, v_dist="uniform"),
+    # other window sizes and head_dim 128 on the stage-1 grid (the K/V-streaming kernel)
+    "stage1_w2x12x12": Workload("stage1_w2x12x12", 1, 4, 180, 360, 8, 64, (2, 12, 12), (1, 6, 6), "bf16", 1),
+    "stage1_h4d128": Workload("stage1_h4d128", 1, 4, 180, 360, 4, 128, (2, 6, 12), (1, 3, 6), "bf16", 1),
     # FP32-I/O runs of the stage shapes (unrounded float32 draws) for the split-bf16
     # matrix-core path and the exact fp32 path
     "stage1_f32_split": Workload("stage1_f32_split", 1, 4, 180, 360, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 1,

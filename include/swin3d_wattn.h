@@ -85,9 +85,12 @@ typedef struct {
 typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 
 /* Validate *desc and build a plan. Host-only: no device is touched.
- * Supported: dtypes BF16 and F32_SPLIT with head_dim 64, wd*wh*ww = 144 and
- * heads < 65536; dtype F32 with head_dim 32 or 64 and wd*wh*ww <= 256.
- * B*D*H*W must be < 2^31.
+ * Supported: dtype BF16 with head_dim 64 or 128, any window with
+ * wd*wh*ww <= 4096 and heads < 65536 (N = 144 at head_dim 64 runs the
+ * single-tile kernel; every other case streams K and V through LDS in
+ * 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with
+ * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
+ * or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
 int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
@@ -178,7 +181,8 @@ typedef struct {
   int64_t workgroups;       /* workgroups one run launches */
   int32_t threads_per_workgroup;
   int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel,
-                               2 = f32 split-bf16 matrix-core kernel */
+                               2 = f32 split-bf16 matrix-core kernel, 3 = bf16 matrix-core
+                               kernel with K/V streamed through LDS */
 } swin3d_wattn_info_t;
 
 /* Fill *info for a plan. Host-only. Returns 0 or EINVAL. */

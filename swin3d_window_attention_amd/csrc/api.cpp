@@ -86,9 +86,12 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   int32_t kernel = -1, threads = 0;
   if (d.dtype == SWIN3D_WATTN_BF16 || d.dtype == SWIN3D_WATTN_F32_SPLIT) {
-    // the launch grid is (window, head); its second dimension stays below 2^16
+    // the launch grid is (window [x query block], head); its second dimension stays below 2^16
     if (d.head_dim == 64 && N == 144 && d.heads < 65536) {
       kernel = d.dtype == SWIN3D_WATTN_BF16 ? 1 : 2;
+      threads = 256;
+    } else if (d.dtype == SWIN3D_WATTN_BF16 && (d.head_dim == 64 || d.head_dim == 128) && d.heads < 65536) {
+      kernel = 3;  // K and V streamed through LDS in 64-key chunks
       threads = 256;
     }
   } else {
@@ -102,6 +105,10 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   int64_t elems = tokens * d.heads * d.head_dim;
   int64_t n_windows = (int64_t)d.B * nwin[0] * nwin[1] * nwin[2];
   int64_t workgroups = n_windows * d.heads;
+  if (kernel == 3) {
+    if (n_windows * ceil_div(N, 64) >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+    workgroups = n_windows * ceil_div(N, 64) * d.heads;
+  }
   if (workgroups >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
 
   // masked-window count (windows needing the region / padding path)
@@ -229,6 +236,7 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
     return SWIN3D_WATTN_EINVAL;
   const int e = plan->kernel == 1   ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
                 : plan->kernel == 2 ? wattn_launch_f32x3(plan, q, k, v, o, st, stream)
+                : plan->kernel == 3 ? wattn_launch_stream(plan, q, k, v, o, st, stream)
                                     : wattn_launch_f32(plan, q, k, v, o, st, stream);
   return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }

@@ -1,0 +1,433 @@
+// Swin3D shifted-window attention for any window size and head_dim 64 or
+// 128, BF16 I/O, K and V streamed through LDS, for gfx950 (MI355X).
+//
+// The Flash-Aurora README ("CuTe DSL window attention") keeps K and V of a
+// whole window in one shared-memory tile when it fits and otherwise falls
+// back to a multi-stage variant that streams K/V through double-buffered
+// shared memory. The N = 144, head_dim 64 production shape has its own
+// single-tile kernel; this one serves every other window and head_dim 128.
+//
+// Work: one workgroup of four waves per (window, head, block of 64 query
+// slots); each wave owns 16 queries. K and V of the window pass through LDS
+// in chunks of 64 key slots, double-buffered: while the waves work on chunk
+// c, each thread holds its part of chunk c + 1 in registers and writes it to
+// the other buffer afterwards (one barrier per chunk). Softmax is online in
+// FP32 (log2 domain): running max m and sum l per query, O rescaled by
+// 2^((m_old - m_new) c2) whenever the max grows.
+//
+// The index map, the stand-in token for padding slots, the shifted-window
+// bias and the padding exclusion as an extra matrix-core k-step, and the
+// MFMA layouts (S^T = K Q^T, O^T = V^T P^T with transposing LDS reads) are
+// those of the single-tile bf16 kernel. Slots beyond N in the last chunk or
+// query block are padding as well.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(8)));
+typedef short short4_t __attribute__((__vector_size__(8)));
+typedef float floatx4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+
+// Matrix-core ordering: consecutive MFMAs use independent accumulators (an
+// MFMA whose accumulator input comes from one of the last few MFMAs reads
+// its A/B registers late) and the order is pinned.
+#define ST_PIN_MFMA() __builtin_amdgcn_sched_barrier(0x7F6)
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQB = 16 * kWaves;  // query slots per workgroup
+constexpr int kKC = 64;           // key slots per chunk
+constexpr int kKT = kKC / 16;     // key tiles per chunk
+constexpr uint32_t kPadSlot = 8;
+
+template <int DH>
+struct Lds {
+  static constexpr int kRow = DH * 2;                // bytes per bf16 row
+  static constexpr int kTile = kKC * kRow;           // one chunk of K (or V)
+  static constexpr int kBuf = 2 * kTile + kKC;       // K, V and the chunk's region codes
+  static constexpr int kXt = 2 * kBuf;               // key feature table
+  static constexpr int kQt = kXt + 9 * 4 * 16;       // query feature table
+  static constexpr int kBytes = kQt + 9 * 4 * 16;
+};
+
+struct FastDiv {
+  uint32_t mul, shr;
+};
+
+// floor(n / d) for 0 <= n < 2^31 (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint32_t shr = 31 + l;
+  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
+}
+
+struct StreamParams {
+  int32_t X[3], P[3], shift[3], win[3], nwin[3];
+  int32_t special[3][3];
+  int32_t N;       // slots per window
+  int32_t nqb;     // query blocks per window
+  int32_t nchunk;  // key chunks per window
+  FastDiv div_qb;  // by query blocks per window
+  FastDiv div_b, div_d, div_h;
+  FastDiv div_hw, div_w;
+  int64_t sq, sk, sv, so;
+  float c2;
+  uint32_t beta01, beta2, pad;
+};
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
+// byte offset of 16-byte chunk c of row r; the XOR touches the low three bits of c only
+template <int DH>
+__device__ __forceinline__ int row_off(int r, int c) { return r * (DH * 2) + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
+
+__device__ __forceinline__ float wave_max16x4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum16x4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+struct WinPos {
+  int b, k[3];
+  bool masked;
+};
+
+__device__ __forceinline__ WinPos decode_window(const StreamParams& p, uint32_t w) {
+  WinPos it;
+  const uint32_t per_d = (uint32_t)(p.nwin[1] * p.nwin[2]);
+  it.b = (int)fdiv(w, p.div_b);
+  w -= (uint32_t)it.b * per_d * (uint32_t)p.nwin[0];
+  it.k[0] = (int)fdiv(w, p.div_d);
+  w -= (uint32_t)it.k[0] * per_d;
+  it.k[1] = (int)fdiv(w, p.div_h);
+  it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
+  bool m = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
+  it.masked = m;
+  return it;
+}
+
+// Slot n of the window -> token (padding and slots >= N: a real stand-in
+// token whose key weight is 0 and whose query is not written) and region code.
+__device__ __forceinline__ void map_slot(const StreamParams& p, const WinPos& it, uint32_t n, int32_t& tok,
+                                         uint32_t& code) {
+  const bool beyond = n >= (uint32_t)p.N;
+  n = beyond ? 0u : n;
+  int o[3];
+  o[0] = (int)fdiv(n, p.div_hw);
+  const uint32_t r = n - (uint32_t)o[0] * (uint32_t)(p.win[1] * p.win[2]);
+  o[1] = (int)fdiv(r, p.div_w);
+  o[2] = (int)(r - (uint32_t)o[1] * (uint32_t)p.win[2]);
+  int g[3];
+  uint32_t c = 0;
+  bool valid = !beyond;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int pa = it.k[a] * p.win[a] + o[a];
+    int ga = pa + p.shift[a];
+    ga = ga >= p.P[a] ? ga - p.P[a] : ga;
+    valid = valid && ga < p.X[a];
+    g[a] = min(ga, p.X[a] - 1);
+    c |= (p.shift[a] > 0 && pa >= p.P[a] - p.shift[a]) ? (1u << a) : 0u;
+  }
+  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
+  code = valid ? c : kPadSlot;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
+__device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
+  typedef short4_t __attribute__((address_space(3))) * lds_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(smem + byte_off));
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             uint16_t* __restrict__ o, const StreamParams p) {
+  using L = Lds<DH>;
+  constexpr int kS = DH / 32;                          // 32-dim k-steps of Q K^T
+  constexpr int kT = DH / 16;                          // 16-dim output tiles
+  constexpr int kCh = DH / 8;                          // 16-byte chunks per row
+  constexpr int kLoads = kKC * kCh / kThreads;         // 16-byte loads per thread per tensor and chunk
+  static_assert(kKC * kCh % kThreads == 0, "whole loads per thread");
+  __shared__ __align__(16) uint8_t smem[L::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const int head = blockIdx.y;
+  const uint32_t wq = fdiv(blockIdx.x, p.div_qb);
+  const int qb = (int)(blockIdx.x - wq * (uint32_t)p.nqb);
+  const WinPos cur = decode_window(p, wq);
+  const size_t hoff = (size_t)head * DH;
+
+  // ---- this wave's 16 queries: Q operands (lane (g4, query l16): dims
+  // 32 s + 8 g4 .. + 7), region code, token ----
+  const int qslot = qb * kQB + wave * 16 + l16;
+  int32_t qtok;
+  uint32_t qcode;
+  map_slot(p, cur, (uint32_t)qslot, qtok, qcode);
+  bf16x8_t qop[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+    qop[s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok * p.sq + hoff + 32 * s + 8 * g4));
+
+  // ---- chunk loader: thread tid moves 16-byte pieces tid + 256 i of K and V
+  // (piece -> key row piece / kCh, chunk piece % kCh) ----
+  u32x4 kr[kLoads], vr[kLoads];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int piece = tid + kThreads * i;
+      int32_t t;
+      uint32_t unused;
+      map_slot(p, cur, (uint32_t)(c * kKC + piece / kCh), t, unused);
+      kr[i] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
+      vr[i] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
+    }
+  };
+
+  // mask-feature tables: also unmasked windows use them when the last chunk
+  // runs past N
+  if (tid < 72) {
+    const int e = tid;
+    const uint32_t ck = (e < 36 ? e : e - 36) >> 2, part = e & 3;
+    u32x4 w = u32x4{0, 0, 0, 0};
+    if (e < 36) {
+      const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
+      if (ck == kPadSlot) {
+        if (part == 3) w[0] = p.pad;
+      } else if (part < 3) {
+        const uint32_t bt = beta[part];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = (uint32_t)(2 * i) != ck ? bt : 0u;
+          const uint32_t hi = (uint32_t)(2 * i + 1) != ck ? bt : 0u;
+          w[i] = lo | (hi << 16);
+        }
+      }
+    } else if (part < 3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = ((uint32_t)(2 * i) == ck ? 0x3F80u : 0u) | ((uint32_t)(2 * i + 1) == ck ? 0x3F800000u : 0u);
+    } else {
+      w[0] = 0x3F80u;
+    }
+    *reinterpret_cast<u32x4*>(smem + L::kXt + e * 16) = w;
+  }
+  // region code of key slot c * kKC + r
+  auto code_of = [&](int c, int r) {
+    int32_t t;
+    uint32_t code;
+    map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
+    return code;
+  };
+
+  // chunk 0 into buffer 0
+  fetch(0);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int piece = tid + kThreads * i;
+    const int r = piece / kCh, c = piece % kCh;
+    *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, c)) = kr[i];
+    *reinterpret_cast<u32x4*>(smem + L::kTile + row_off<DH>(r, c)) = vr[i];
+  }
+  if (tid < kKC) smem[2 * L::kTile + tid] = (uint8_t)code_of(0, tid);
+  __syncthreads();
+
+  const float c2 = p.c2;
+  float m = -INFINITY, l = 0.f;
+  floatx4 O[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t qxb = *reinterpret_cast<const bf16x8_t*>(smem + L::kQt + (qcode * 4 + g4) * 16);
+  const int e = l16 >> 2, qd = l16 & 3;
+
+  for (int c = 0; c < p.nchunk; ++c) {
+    const int buf = c & 1;
+    const uint8_t* kb = smem + buf * L::kBuf;
+    const uint8_t* vb = kb + L::kTile;
+    const uint8_t* cb = kb + 2 * L::kTile;
+    const bool more = c + 1 < p.nchunk;
+    if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
+
+    // ---- S^T = K Q^T for this chunk's four key tiles ----
+    floatx4 S[kKT];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      bf16x8_t kf[kKT];
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
+        kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[s], S[kt], 0, 0, 0);
+        ST_PIN_MFMA();
+      }
+    }
+    // mask k-step: the window has a cut or padding, or this chunk runs past N
+    if (cur.masked || (c + 1) * kKC > p.N) {
+      bf16x8_t xf[kKT];
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
+        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
+        ST_PIN_MFMA();
+      }
+    }
+
+    // ---- online softmax ----
+    float mc = S[0][0];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, S[kt][i]);
+    const float m_new = fmaxf(m, wave_max16x4(mc));
+    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);  // 0 on the first chunk
+    const float nm = -m_new * c2;
+    floatx4 P[kKT];
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
+        rs += P[kt][i];
+      }
+    l = l * alpha + wave_sum16x4(rs);
+    m = m_new;
+#pragma unroll
+    for (int t = 0; t < kT; ++t) O[t] *= alpha;
+    bf16x8_t Pb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      Pb[j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
+                                      __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
+
+    // ---- O^T += V^T P^T over the chunk's two 32-key steps ----
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 vf[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        const int d = dbase(t, qd);
+        const int lo_off = (32 * j + 4 * g4 + e) * (DH * 2) + ((((d >> 3) ^ swz(32 * j + 4 * g4 + e))) << 4) + ((d & 4) << 1);
+        const int hi_off = (32 * j + 16 + 4 * g4 + e) * (DH * 2) + ((((d >> 3) ^ swz(32 * j + 16 + 4 * g4 + e))) << 4) + ((d & 4) << 1);
+        const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
+        const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
+        vf[t] = u32x4{a[0], a[1], b[0], b[1]};
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[j], O[t], 0, 0, 0);
+        ST_PIN_MFMA();
+      }
+    }
+
+    // ---- next chunk into the other buffer (everyone finished chunk c - 1,
+    // the last reader of that buffer, at the previous barrier) ----
+    if (more) {
+      uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int piece = tid + kThreads * i;
+        const int r = piece / kCh, cc = piece % kCh;
+        *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, cc)) = kr[i];
+        *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, cc)) = vr[i];
+      }
+      if (tid < kKC) nb[2 * L::kTile + tid] = (uint8_t)code_of(c + 1, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- normalise and scatter (queries of the window only) ----
+  if (qcode != kPadSlot) {
+    const float inv = 1.0f / l;
+    uint16_t* out = o + (size_t)qtok * p.so + hoff;
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+      const bf16x4_t w = __builtin_convertvector(O[t] * inv, bf16x4_t);
+      *reinterpret_cast<u32x2*>(out + dbase(t, g4)) = __builtin_bit_cast(u32x2, w);
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+                  const swin3d_wattn_strides_t* st, hipStream_t s) {
+  StreamParams p;
+  const swin3d_wattn_desc_t& d = pl->desc;
+  p.X[0] = d.D;
+  p.X[1] = d.H;
+  p.X[2] = d.W;
+  for (int a = 0; a < 3; ++a) {
+    p.P[a] = pl->padded[a];
+    p.shift[a] = d.shift[a];
+    p.win[a] = d.window[a];
+    p.nwin[a] = pl->nwin[a];
+    for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
+  }
+  p.N = pl->N;
+  p.nqb = (pl->N + kQB - 1) / kQB;
+  p.nchunk = (pl->N + kKC - 1) / kKC;
+  p.div_qb = make_fastdiv((uint32_t)p.nqb);
+  p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
+  p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
+  p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
+  p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
+  p.div_w = make_fastdiv((uint32_t)d.window[2]);
+  p.sq = st->q;
+  p.sk = st->k;
+  p.sv = st->v;
+  p.so = st->o;
+  p.c2 = pl->c2;
+  p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
+  p.beta2 = pl->beta_bf16[2];
+  p.pad = pl->pad_bf16;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  void* args[] = {&qq, &kk, &vv, &oo, &p};
+  const dim3 grid((unsigned)(pl->n_windows * p.nqb), (unsigned)d.heads);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH>), grid, dim3(kThreads), args, 0, s);
+}
+
+}  // namespace
+
+int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                        const swin3d_wattn_strides_t* stride, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = p->desc.head_dim == 128 ? launch<128>(p, q, k, v, o, stride, s)
+                                               : launch<64>(p, q, k, v, o, stride, s);
+  return (int)e;
+}

@@ -87,7 +87,7 @@ def test_masked_window_count_matches_oracle_labels():
     (dict(shift=(1, 6, 6)), -1), (dict(dtype=7), -1), (dict(scale=float("nan")), -1),
     (dict(scale=float("inf")), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
     (dict(cross_region_bias=float("nan")), -1), (dict(cross_region_bias=1.0), -1),
-    (dict(head_dim=128), -2), (dict(head_dim=32), -2), (dict(window=(2, 6, 6), shift=(1, 3, 3)), -2), (dict(window=(2, 6, 6)), -1),
+    (dict(head_dim=256), -2), (dict(head_dim=32), -2), (dict(head_dim=96), -2), (dict(window=(2, 6, 6)), -1),
     (dict(window=(4, 8, 12), shift=(1, 3, 3), dtype="f32", head_dim=64), -2),
     (dict(dtype="f32", head_dim=48), -2),
     (dict(B=2, D=4, H=46341, W=46341), -2),
@@ -96,6 +96,22 @@ def test_masked_window_count_matches_oracle_labels():
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)
     assert rc == code and h is None
+
+
+def test_streaming_plans():
+    """bf16 windows other than 144 slots, or head_dim 128, go to the K/V-streaming kernel (3)."""
+    for kw, wg in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 2 * 8),     # N = 72: 2 query blocks
+                   (dict(head_dim=128), 1800 * 3 * 8),                          # N = 144: 3 query blocks
+                   (dict(window=(4, 12, 24), shift=(2, 6, 12)), 225 * 18 * 8),  # N = 1152
+                   (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8)]:
+        rc, h = _create(**kw)
+        assert rc == 0, kw
+        rc2, info = sw.swin3d_wattn_get_info(h)
+        assert info.kernel == 3 and info.workgroups == wg, (kw, info.kernel, info.workgroups)
+        sw.swin3d_wattn_destroy(h)
+    rc, h = _create()
+    assert sw.swin3d_wattn_get_info(h)[1].kernel == 1  # the production shape keeps its own kernel
+    sw.swin3d_wattn_destroy(h)
 
 
 def test_f32_split_plans():
