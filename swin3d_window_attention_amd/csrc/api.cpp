@@ -106,8 +106,10 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   int64_t n_windows = (int64_t)d.B * nwin[0] * nwin[1] * nwin[2];
   int64_t workgroups = n_windows * d.heads;
   if (kernel == 3) {
-    if (n_windows * ceil_div(N, 64) >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
-    workgroups = n_windows * ceil_div(N, 64) * d.heads;
+    // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of 64
+    const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, 64);
+    if (gx >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+    workgroups = gx * d.heads;
   }
   if (workgroups >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
 

@@ -78,6 +78,7 @@ struct StreamParams {
   int32_t N;       // slots per window
   int32_t nqb;     // query blocks per window
   int32_t nchunk;  // key chunks per window
+  int32_t n_windows;
   FastDiv div_qb;  // by query blocks per window
   FastDiv div_b, div_d, div_h;
   FastDiv div_hw, div_w;
@@ -181,8 +182,14 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int head = blockIdx.y;
-  const uint32_t wq = fdiv(blockIdx.x, p.div_qb);
-  const int qb = (int)(blockIdx.x - wq * (uint32_t)p.nqb);
+  // XCD-aware order: workgroup x runs on XCD x % 8, so x = 8 (w_hi nqb + qb) + w_lo
+  // gives window 8 w_hi + w_lo all its query blocks on one XCD, one after the
+  // other, where they share that XCD's L2 copy of the window's K and V
+  const uint32_t xk = blockIdx.x >> 3;
+  const uint32_t w_hi = fdiv(xk, p.div_qb);
+  const int qb = (int)(xk - w_hi * (uint32_t)p.nqb);
+  const uint32_t wq = 8 * w_hi + (blockIdx.x & 7);
+  if (wq >= (uint32_t)p.n_windows) return;  // grid padded to a multiple of 8 windows
   const WinPos cur = decode_window(p, wq);
   const size_t hoff = (size_t)head * DH;
 
@@ -399,6 +406,7 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   p.N = pl->N;
   p.nqb = (pl->N + kQB - 1) / kQB;
   p.nchunk = (pl->N + kKC - 1) / kKC;
+  p.n_windows = (int32_t)pl->n_windows;
   p.div_qb = make_fastdiv((uint32_t)p.nqb);
   p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
   p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
@@ -418,7 +426,7 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-  const dim3 grid((unsigned)(pl->n_windows * p.nqb), (unsigned)d.heads);
+  const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)d.heads);
   return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH>), grid, dim3(kThreads), args, 0, s);
 }
 
