@@ -91,8 +91,9 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
       kernel = d.dtype == SWIN3D_WATTN_BF16 ? 1 : 2;
       threads = 256;
     } else if (d.dtype == SWIN3D_WATTN_BF16 && (d.head_dim == 64 || d.head_dim == 128) && d.heads < 65536) {
-      kernel = 3;  // K and V streamed through LDS in 64-key chunks
-      threads = 256;
+      kernel = 3;  // K and V streamed through LDS
+      // block shape: 3 waves / 48-key chunks where that wastes no slot and 64 would, else 4 / 64
+      threads = (N % 64 != 0 && N % 48 == 0) ? 192 : 256;
     }
   } else {
     if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
@@ -106,8 +107,9 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   int64_t n_windows = (int64_t)d.B * nwin[0] * nwin[1] * nwin[2];
   int64_t workgroups = n_windows * d.heads;
   if (kernel == 3) {
-    // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of 64
-    const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, 64);
+    // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of
+    // 16 slots per wave
+    const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, threads / 4);
     if (gx >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
     workgroups = gx * d.heads;
   }

@@ -7,11 +7,14 @@
 // shared memory. The N = 144, head_dim 64 production shape has its own
 // single-tile kernel; this one serves every other window and head_dim 128.
 //
-// Work: one workgroup of four waves per (window, head, block of 64 query
-// slots); each wave owns 16 queries. K and V of the window pass through LDS
-// in chunks of 64 key slots, double-buffered: while the waves work on chunk
-// c, each thread holds its part of chunk c + 1 in registers and writes it to
-// the other buffer afterwards (one barrier per chunk). Softmax is online in
+// Work: one workgroup per (window, head, block of query slots), 16 queries
+// per wave; K and V of the window pass through LDS in chunks of key slots,
+// double-buffered: while the waves work on chunk c, each thread holds its
+// part of chunk c + 1 in registers and writes it to the other buffer
+// afterwards (one barrier per chunk). Two block shapes: four waves and
+// 64-key chunks, or, where the window size is a multiple of 48 but not of
+// 64 (144, 288, ...), three waves and 48-key chunks, so that no query or
+// key slot past the window is processed. Softmax is online in
 // FP32 (log2 domain): running max m and sum l per query, O rescaled by
 // 2^((m_old - m_new) c2) whenever the max grows.
 //
@@ -39,18 +42,13 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 // its A/B registers late) and the order is pinned.
 #define ST_PIN_MFMA() __builtin_amdgcn_sched_barrier(0x7F6)
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 16 * kWaves;  // query slots per workgroup
-constexpr int kKC = 64;           // key slots per chunk
-constexpr int kKT = kKC / 16;     // key tiles per chunk
 constexpr uint32_t kPadSlot = 8;
 
-template <int DH>
+template <int DH, int KC>
 struct Lds {
   static constexpr int kRow = DH * 2;                // bytes per bf16 row
-  static constexpr int kTile = kKC * kRow;           // one chunk of K (or V)
-  static constexpr int kBuf = 2 * kTile + kKC;       // K, V and the chunk's region codes
+  static constexpr int kTile = KC * kRow;            // one chunk of K (or V)
+  static constexpr int kBuf = 2 * kTile + 64;        // K, V and the chunk's region codes
   static constexpr int kXt = 2 * kBuf;               // key feature table
   static constexpr int kQt = kXt + 9 * 4 * 16;       // query feature table
   static constexpr int kBytes = kQt + 9 * 4 * 16;
@@ -163,17 +161,24 @@ __device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(smem + byte_off));
 }
 
-template <int DH>
-__global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v,
-                                                             uint16_t* __restrict__ o, const StreamParams p) {
-  using L = Lds<DH>;
+template <int DH, int WAVES, int KC>
+__global__ __launch_bounds__(64 * WAVES) void wattn_stream_item(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ o, const StreamParams p) {
+  using L = Lds<DH, KC>;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kQB = 16 * WAVES;                      // query slots per workgroup
+  constexpr int kKC = KC;                              // key slots per chunk
+  constexpr int kKT = KC / 16;                         // key tiles per chunk
+  constexpr int kJ = KC / 32;                          // whole 32-key steps of P V
+  constexpr bool kTail = KC % 32 != 0;                 // plus one 16-key step
   constexpr int kS = DH / 32;                          // 32-dim k-steps of Q K^T
   constexpr int kT = DH / 16;                          // 16-dim output tiles
   constexpr int kCh = DH / 8;                          // 16-byte chunks per row
   constexpr int kLoads = kKC * kCh / kThreads;         // 16-byte loads per thread per tensor and chunk
   static_assert(kKC * kCh % kThreads == 0, "whole loads per thread");
+  static_assert(KC % 16 == 0 && KC <= 64 && kThreads >= 72, "chunk and table sizes");
   __shared__ __align__(16) uint8_t smem[L::kBytes];
 
   const int tid = threadIdx.x;
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
   for (int s = 0; s < kS; ++s)
     qop[s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok * p.sq + hoff + 32 * s + 8 * g4));
 
-  // ---- chunk loader: thread tid moves 16-byte pieces tid + 256 i of K and V
+  // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
   // (piece -> key row piece / kCh, chunk piece % kCh) ----
   u32x4 kr[kLoads], vr[kLoads];
   auto fetch = [&](int c) {
@@ -283,10 +288,15 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
     const bool more = c + 1 < p.nchunk;
     if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
 
-    // ---- S^T = K Q^T for this chunk's four key tiles ----
-    floatx4 S[kKT];
+    // ---- S^T = K Q^T for this chunk's key tiles. With fewer than four key
+    // tiles, even and odd k-steps accumulate separately, so that no MFMA
+    // takes its accumulator from one of the three before it ----
+    constexpr int kAcc = kKT >= 4 ? 1 : 2;
+    floatx4 S2[kAcc][kKT];
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < kAcc; ++a)
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) S2[a][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
       bf16x8_t kf[kKT];
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
         kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[s], S[kt], 0, 0, 0);
+        S2[s % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[s], S2[s % kAcc][kt], 0, 0, 0);
         ST_PIN_MFMA();
       }
     }
@@ -307,10 +317,13 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
         xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S[kt], 0, 0, 0);
+        S2[kS % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S2[kS % kAcc][kt], 0, 0, 0);
         ST_PIN_MFMA();
       }
     }
+    floatx4 S[kKT];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][kt] : S2[0][kt] + S2[kAcc - 1][kt];
 
     // ---- online softmax ----
     float mc = S[0][0];
@@ -334,15 +347,16 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
     m = m_new;
 #pragma unroll
     for (int t = 0; t < kT; ++t) O[t] *= alpha;
-    bf16x8_t Pb[2];
+    bf16x8_t Pb[kJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kJ; ++j)
       Pb[j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
                                       __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x4_t Pt = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
 
     // ---- O^T += V^T P^T over the chunk's two 32-key steps ----
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kJ; ++j) {
       u32x4 vf[kT];
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
@@ -356,6 +370,20 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
         O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[j], O[t], 0, 0, 0);
+        ST_PIN_MFMA();
+      }
+    }
+    if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
+      short4_t vt[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        const int d = dbase(t, qd);
+        const int key = 32 * kJ + 4 * g4 + e;
+        vt[t] = lds_tr(vb, key * (DH * 2) + (((d >> 3) ^ swz(key)) << 4) + ((d & 4) << 1));
+      }
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
         ST_PIN_MFMA();
       }
     }
@@ -388,9 +416,11 @@ __global__ __launch_bounds__(kThreads) void wattn_stream_item(const uint16_t* __
   }
 }
 
-template <int DH>
+template <int DH, int WAVES, int KC>
 hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
                   const swin3d_wattn_strides_t* st, hipStream_t s) {
+  constexpr int kQB = 16 * WAVES;
+  constexpr int kKC = KC;
   StreamParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
   p.X[0] = d.D;
@@ -427,7 +457,8 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
   const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)d.heads);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH>), grid, dim3(kThreads), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC>), grid,
+                         dim3(64 * WAVES), args, 0, s);
 }
 
 }  // namespace
@@ -435,7 +466,11 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
 int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                         const swin3d_wattn_strides_t* stride, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = p->desc.head_dim == 128 ? launch<128>(p, q, k, v, o, stride, s)
-                                               : launch<64>(p, q, k, v, o, stride, s);
+  const bool k48 = p->threads == 192;  // the plan's block shape: 3 waves and 48-key chunks
+  hipError_t e;
+  if (p->desc.head_dim == 128)
+    e = k48 ? launch<128, 3, 48>(p, q, k, v, o, stride, s) : launch<128, 4, 64>(p, q, k, v, o, stride, s);
+  else
+    e = k48 ? launch<64, 3, 48>(p, q, k, v, o, stride, s) : launch<64, 4, 64>(p, q, k, v, o, stride, s);
   return (int)e;
 }

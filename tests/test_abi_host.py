@@ -99,15 +99,18 @@ def test_create_rejects(kw, code):
 
 
 def test_streaming_plans():
-    """bf16 windows other than 144 slots, or head_dim 128, go to the K/V-streaming kernel (3)."""
-    for kw, wg in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 2 * 8),     # N = 72: 2 query blocks
-                   (dict(head_dim=128), 1800 * 3 * 8),                          # N = 144: 3 query blocks
-                   (dict(window=(4, 12, 24), shift=(2, 6, 12)), 232 * 18 * 8),  # N = 1152, 225 -> 232 windows
-                   (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8)]:
+    """bf16 windows other than 144 slots, or head_dim 128, go to the K/V-streaming kernel (3):
+    3 waves and 48-slot blocks where N is a multiple of 48 but not of 64, else 4 waves and 64."""
+    for kw, wg, thr in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 2 * 8, 256),     # N = 72
+                        (dict(head_dim=128), 1800 * 3 * 8, 192),                          # N = 144: 3 x 48
+                        (dict(window=(2, 12, 12), shift=(1, 6, 6)), 904 * 6 * 8, 192),    # N = 288: 6 x 48
+                        (dict(window=(4, 12, 24), shift=(2, 6, 12)), 232 * 18 * 8, 256),  # N = 1152 = 18 x 64
+                        (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8, 256)]:
         rc, h = _create(**kw)
         assert rc == 0, kw
         rc2, info = sw.swin3d_wattn_get_info(h)
-        assert info.kernel == 3 and info.workgroups == wg, (kw, info.kernel, info.workgroups)
+        assert (info.kernel, info.workgroups, info.threads_per_workgroup) == (3, wg, thr), (
+            kw, info.kernel, info.workgroups, info.threads_per_workgroup)
         sw.swin3d_wattn_destroy(h)
     rc, h = _create()
     assert sw.swin3d_wattn_get_info(h)[1].kernel == 1  # the production shape keeps its own kernel
