@@ -117,6 +117,53 @@ def copy_calibration(nbytes: int, steps: int):
                       "gbs_read_plus_write": 2 * n * 2 / dt / 1e9}), flush=True)
 
 
+def write_traffic(prof_dir: str, copy_bytes: int = 536870912):
+    """Turn four rocprofv3 --pmc runs into the traffic summary that bench.py reports: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) of the stage-1 kernel, each scaled by what the same counter
+    reads for a plain device copy of copy_bytes (subfolders fetch, write, copyfetch, copywrite
+    of prof_dir, as written by the commands in profiles/wattn_bf16_item_stage1_hbm_traffic.md).
+    Host only; records the SHA-256 of the kernel source the counters were taken on."""
+    import csv
+    import glob
+
+    def mean_counter(sub, counter, name_part):
+        vals = []
+        for f in glob.glob(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            sys.exit(f"bench.py: no {counter} rows for {name_part!r} under {prof_dir}/{sub}")
+        return sum(vals) / len(vals)
+
+    fetch = mean_counter("fetch", "FETCH_SIZE", "wattn_bf16_item")
+    write = mean_counter("write", "WRITE_SIZE", "wattn_bf16_item")
+    cfetch = mean_counter("copyfetch", "FETCH_SIZE", "copyBuffer")
+    cwrite = mean_counter("copywrite", "WRITE_SIZE", "copyBuffer")
+    fscale = copy_bytes / 1024 / cfetch
+    wscale = copy_bytes / 1024 / cwrite
+    import datagen
+    nbytes = algorithmic_work(datagen.WORKLOADS["stage1"])[0]
+    out = {
+        "kernel": "wattn_bf16_item",
+        "workload": "stage-1 latent grid B=1 D=4 H=180 W=360, 8 heads, head_dim 64, window (2,6,12), "
+                    "shift (1,3,6), bf16",
+        "kernel_source": os.path.relpath(KERNEL_SRC, ROOT),
+        "kernel_sha256": kernel_digest(),
+        "fetch_size_kib_per_dispatch": fetch,
+        "write_size_kib_per_dispatch": write,
+        "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_size_kib": cfetch,
+                             "write_size_kib": cwrite, "fetch_scale": fscale, "write_scale": wscale},
+        "read_bytes_per_launch": fetch * 1024 * fscale,
+        "write_bytes_per_launch": write * 1024 * wscale,
+        "traffic_bytes_per_launch": (fetch * fscale + write * wscale) * 1024,
+        "algorithmic_bytes_per_launch": nbytes,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def bench_adaln(args):
     """The fused AdaLN + residual step at the stage-1 token count (one JSON line)."""
     import torch
@@ -186,7 +233,14 @@ def main():
                          "launch and time each launch with its own events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (profiler counter calibration)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="host only: write the stage-1 traffic summary from rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE runs under DIR (fetch, write, copyfetch, copywrite)")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

@@ -88,9 +88,9 @@ typedef struct swin3d_wattn_plan* swin3d_wattn_t;
  * Supported: dtype BF16 with head_dim 64 or 128, any window with
  * wd*wh*ww <= 4096 and heads < 65536 (N = 144 at head_dim 64 runs the
  * single-tile kernel; every other case streams K and V through LDS in
- * 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with
+ * 48- or 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with
  * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
- * or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31.
+ * or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31 and each of D, H, W < 2^24.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
 int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
@@ -122,14 +122,14 @@ typedef struct {
 } swin3d_wattn_strides_t;
 
 /* swin3d_wattn_run with explicit token strides (see swin3d_wattn_strides_t).
- * Each stride must be >= heads*head_dim and a multiple of 16 bytes; the
- * pointers 16-byte aligned. The span of a tensor is the byte range
+ * Each stride must be >= heads*head_dim, below 2^31 elements and a multiple
+ * of 16 bytes; the pointers 16-byte aligned. The span of a tensor is the byte range
  * [ptr, ptr + ((tokens - 1) * stride + heads*head_dim) * element size); the
  * span of O must not overlap the spans of Q, K or V, while Q, K and V may
  * overlap each other. Elements of
  * the O buffer outside the (token, head, dim) positions are never touched.
- * Returns 0, EINVAL (null plan, pointer or strides, a stride too small or
- * misaligned, misalignment, overlap) or ELAUNCH. */
+ * Returns 0, EINVAL (null plan, pointer or strides, a stride too small, too
+ * large or misaligned, misalignment, overlap) or ELAUNCH. */
 int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, const void* k, const void* v, void* o,
                              const swin3d_wattn_strides_t* strides, void* stream);
 

@@ -68,6 +68,9 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   if (std::isnan(d.cross_region_bias) || d.cross_region_bias > 0.0f) return SWIN3D_WATTN_EINVAL;
 
   const int32_t X[3] = {d.D, d.H, d.W};
+  // the kernels' per-lane index arithmetic takes grid extents below 2^24
+  for (int a = 0; a < 3; ++a)
+    if (X[a] >= (1 << 24)) return SWIN3D_WATTN_EUNSUPPORTED;
   int64_t tokens = (int64_t)d.B * d.D * d.H * d.W;
   if (tokens >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
   int64_t padded_tokens = d.B;
@@ -233,7 +236,7 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
   const int64_t s[4] = {st->q, st->k, st->v, st->o};
   int64_t span[4];
   for (int i = 0; i < 4; ++i) {
-    if (s[i] < row || s[i] > (int64_t(1) << 40) || (s[i] * plan->elem_bytes) % 16 != 0) return SWIN3D_WATTN_EINVAL;
+    if (s[i] < row || s[i] >= (int64_t(1) << 31) || (s[i] * plan->elem_bytes) % 16 != 0) return SWIN3D_WATTN_EINVAL;
     span[i] = ((plan->tokens - 1) * s[i] + row) * plan->elem_bytes;
   }
   if (overlaps(o, span[3], q, span[0]) || overlaps(o, span[3], k, span[1]) || overlaps(o, span[3], v, span[2]))

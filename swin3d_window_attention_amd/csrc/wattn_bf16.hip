@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace {
@@ -102,12 +104,26 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
   return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
 }
 
+// The same for the per-lane slot arithmetic, where n < 2^8 (a slot of the
+// 144-token window) and d <= 2^12, with a fixed shift in full-rate 24-bit
+// operations: mul = ceil(2^20 / d) <= 2^20, so n * mul < 2^28, and the error
+// term n * (mul * d - 2^20) < 2^8 * 2^12 stays below 2^20: the quotient is
+// exact, and it is known to fit 12 bits, so it feeds the next 24-bit product
+// unmasked.
+constexpr uint32_t kSmallShr = 20;
+
+uint32_t make_small_div(uint32_t d) { return (uint32_t)(((uint64_t(1) << kSmallShr) + d - 1) / d); }
+
+__device__ __forceinline__ uint32_t fdiv_small(uint32_t n, uint32_t mul) { return __umul24(n, mul) >> kSmallShr; }
+
 struct AttnParams {
   int32_t X[3], P[3], shift[3], win[3], nwin[3];
   int32_t special[3][3];
   FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
-  FastDiv div_hw, div_w;        // by window slots per depth step (wh * ww), per row (ww)
-  int64_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements)
+  uint32_t div_hw, div_w;       // fdiv_small multipliers by wh * ww and by ww
+  uint32_t whw;                 // wh * ww
+  uint32_t plane;               // H * W tokens
+  uint32_t sq, sk, sv, so;      // token strides of Q, K, V, O (elements, < 2^31)
   float c2;
   uint32_t beta01;  // bf16 beta term 0 | term 1 << 16
   uint32_t beta2;   // bf16 beta term 2
@@ -130,6 +146,9 @@ __device__ __forceinline__ float wave_max16x4(float x) {
 
 struct WinPos {
   int b, k[3];
+  int base[3];    // first padded-grid coordinate of the window, k * w
+  uint32_t tokb;  // first token of batch element b
+  uint32_t tok0;  // token of slot 0 when the window has no cut and no padding
   bool masked;
 };
 
@@ -144,42 +163,61 @@ __device__ __forceinline__ WinPos decode_window(const AttnParams& p, uint32_t w)
   w -= (uint32_t)it.k[0] * per_d;
   it.k[1] = (int)fdiv(w, p.div_h);
   it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
+  for (int a = 0; a < 3; ++a) it.base[a] = it.k[a] * p.win[a];
+  it.tokb = (uint32_t)it.b * (uint32_t)p.X[0] * p.plane;
   bool m = false;
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
     for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
   it.masked = m;
+  // without a cut or padding on any axis no slot wraps or falls outside the
+  // grid, so slot (od, oh, ow) is token tok0 + od H W + oh W + ow
+  it.tok0 = it.tokb + (uint32_t)(it.base[0] + p.shift[0]) * p.plane +
+            (uint32_t)(it.base[1] + p.shift[1]) * (uint32_t)p.X[2] + (uint32_t)(it.base[2] + p.shift[2]);
   return it;
 }
 
-// Grid position of slot n = (od, oh, ow) (row-major inside the window) and
-// its region code (one bit per axis: shifted axis and position in the
-// wrapped part [P - s, P)), or kPadSlot for padding. A padding slot still
-// gets a real token, the nearest one on the grid (each coordinate clamped to
-// X - 1), so that all loads can be unconditional.
+// Grid position of slot n = (od, oh, ow) (row-major inside the window, n <
+// 2^8) and its region code (one bit per axis: position in the wrapped part
+// [P - s, P), empty when s = 0), or kPadSlot for padding. A padding slot
+// still gets a real token, the nearest one on the grid (each coordinate
+// clamped to X - 1), so that all loads can be unconditional. Per lane this
+// is full-rate 24-bit arithmetic except one 32-bit product (g0 * H * W).
+// kEdge = false is the shortcut for windows without a cut or padding
+// (it.masked false, a wave-uniform condition): every code is 0 there.
+template <bool kEdge>
 __device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, uint32_t n, int32_t& tok,
                                          uint32_t& code) {
-  int o[3];
-  o[0] = (int)fdiv(n, p.div_hw);
-  const uint32_t r = n - (uint32_t)o[0] * (uint32_t)(p.win[1] * p.win[2]);
-  o[1] = (int)fdiv(r, p.div_w);
-  o[2] = (int)(r - (uint32_t)o[1] * (uint32_t)p.win[2]);
+  uint32_t o[3];
+  o[0] = fdiv_small(n, p.div_hw);
+  const uint32_t r = n - __umul24(o[0], p.whw);
+  o[1] = fdiv_small(r, p.div_w);
+  o[2] = r - __umul24(o[1], (uint32_t)p.win[2]);
+  if (!kEdge) {
+    tok = (int32_t)(it.tok0 + o[0] * p.plane + __umul24(o[1], (uint32_t)p.X[2]) + o[2]);
+    code = 0;
+    return;
+  }
   int g[3];
   uint32_t c = 0;
   bool valid = true;
 #pragma unroll
   for (int a = 0; a < 3; ++a) {
-    const int pa = it.k[a] * p.win[a] + o[a];
+    const int pa = it.base[a] + (int)o[a];
     int ga = pa + p.shift[a];
     ga = ga >= p.P[a] ? ga - p.P[a] : ga;
     valid = valid && ga < p.X[a];
     g[a] = min(ga, p.X[a] - 1);
-    c |= (p.shift[a] > 0 && pa >= p.P[a] - p.shift[a]) ? (1u << a) : 0u;
+    c |= pa >= p.P[a] - p.shift[a] ? (1u << a) : 0u;
   }
-  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
+  tok = (int32_t)(it.tokb + (uint32_t)g[0] * p.plane + __umul24((uint32_t)g[1], (uint32_t)p.X[2]) + (uint32_t)g[2]);
   code = valid ? c : kPadSlot;
 }
+
+// element offset of token t's row in a tensor of token stride s (< 2^31):
+// added to a per-lane column pointer, one 32 x 32 + 64-bit multiply-add
+__device__ __forceinline__ size_t row_off(int32_t t, uint32_t s) { return (uint64_t)(uint32_t)t * s; }
 
 // Q, K and V rows are read exactly once: a non-temporal load marks the
 // line as streaming, so it does not displace useful lines in L2 or the
@@ -219,7 +257,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // one head of many neighbouring windows
   const int head = blockIdx.y;
   const WinPos cur = decode_window(p, blockIdx.x);
-  const size_t hoff = (size_t)head * 64;
+  const uint32_t hoff = (uint32_t)head * 64;
 
   // ---- gather first: each thread maps the slots it loads itself, so the
   // loads leave before any table or barrier. K and V rows go to registers
@@ -229,33 +267,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int kChunks = kN * 8;
   constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
   u32x4 kr[kPer], vr[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int c = tid + kThreads * j;
-    if (c < kChunks) {
-      int32_t t;
-      uint32_t unused;
-      map_slot(p, cur, (uint32_t)(c >> 3), t, unused);
-      kr[j] = ldg16(k + (size_t)t * p.sk + hoff + (c & 7) * 8);
-      vr[j] = ldg16(v + (size_t)t * p.sv + hoff + (c & 7) * 8);
-    }
-  }
+  // every load of a thread reads 16-byte chunk tid % 8 (K, V) or lane % 8 (Q)
+  // of its row: the same column, tid % 8 = lane % 8
+  const uint32_t col = hoff + 8 * (uint32_t)(tid & 7);
+  const uint16_t* kcol = k + col;
+  const uint16_t* vcol = v + col;
+  const uint16_t* qcol = q + col;
+  uint16_t* ocol = o + col;  // the output stores write chunk lane % 8 too
   // Q rows of this wave's tiles are read whole: load s of a tile covers its
   // rows 8 s .. 8 s + 7, lane L reading 16-byte chunk L % 8 of row 8 s + L / 8
   u32x4 qr[kMaxQT][2];
+  auto gather = [&](auto edge) {
+    constexpr bool kEdge = decltype(edge)::value;
 #pragma unroll
-  for (int qi = 0; qi < kMaxQT; ++qi) {
-    const int qt = wave + kWaves * qi;
-    if (qt < kNT) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
+    for (int j = 0; j < kPer; ++j) {
+      const int c = tid + kThreads * j;
+      if (c < kChunks) {
         int32_t t;
         uint32_t unused;
-        map_slot(p, cur, (uint32_t)(qt * 16 + 8 * s + (lane >> 3)), t, unused);
-        qr[qi][s] = ldg16(q + (size_t)t * p.sq + hoff + 8 * (lane & 7));
+        map_slot<kEdge>(p, cur, (uint32_t)(c >> 3), t, unused);
+        kr[j] = ldg16(kcol + row_off(t, p.sk));
+        vr[j] = ldg16(vcol + row_off(t, p.sv));
       }
     }
-  }
+#pragma unroll
+    for (int qi = 0; qi < kMaxQT; ++qi) {
+      const int qt = wave + kWaves * qi;
+      if (qt < kNT) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          int32_t t;
+          uint32_t unused;
+          map_slot<kEdge>(p, cur, (uint32_t)(qt * 16 + 8 * s + (lane >> 3)), t, unused);
+          qr[qi][s] = ldg16(qcol + row_off(t, p.sq));
+        }
+      }
+    }
+  };
+  // one uniform branch: windows without a cut or padding take the shortcut
+  if (cur.masked)
+    gather(std::true_type{});
+  else
+    gather(std::false_type{});
 
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -269,7 +322,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   for (int r = tid; r < kN; r += kThreads) {
     int32_t t;
     uint32_t c;
-    map_slot(p, cur, (uint32_t)r, t, c);
+    if (cur.masked)
+      map_slot<true>(p, cur, (uint32_t)r, t, c);
+    else
+      map_slot<false>(p, cur, (uint32_t)r, t, c);
     tokS[r] = t;
     codeS[r] = (uint8_t)c;
   }
@@ -459,7 +515,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         val[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)(mine ? c0[d] : z[d]));
       const int r = qt * 16 + 8 * s + rr;
       if (codeS[r] != kPadSlot)
-        *reinterpret_cast<u32x4*>(o + (size_t)tokS[r] * p.so + hoff + 8 * ch) = val;
+        *reinterpret_cast<u32x4*>(ocol + row_off(tokS[r], p.so)) = val;
     }
   }
 }
@@ -485,12 +541,14 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
   p.pad = pl->pad_bf16;
-  p.sq = st->q;
-  p.sk = st->k;
-  p.sv = st->v;
-  p.so = st->o;
-  p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
-  p.div_w = make_fastdiv((uint32_t)d.window[2]);
+  p.sq = (uint32_t)st->q;
+  p.sk = (uint32_t)st->k;
+  p.sv = (uint32_t)st->v;
+  p.so = (uint32_t)st->o;
+  p.whw = (uint32_t)(d.window[1] * d.window[2]);
+  p.plane = (uint32_t)(d.H * d.W);
+  p.div_hw = make_small_div(p.whw);
+  p.div_w = make_small_div((uint32_t)d.window[2]);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);

@@ -181,6 +181,7 @@ def test_run_strided_rejects_before_launch():
     assert run(q, k, v, o, S(row - 8, 3 * row, 3 * row, row)) == -1      # stride below a token
     assert run(q, k, v, o, S(3 * row + 4, 3 * row, 3 * row, row)) == -1  # 8 bytes: not 16-aligned
     assert run(q, k, v, o, S(3 * row, 3 * row, 3 * row, 0)) == -1
+    assert run(q, k, v, o, S(3 * row, 1 << 31, 3 * row, row)) == -1     # stride of 2^31 elements
     assert run(q, k, v, o + 8, fused) == -1                              # misaligned pointer
     assert sw.load_library().swin3d_wattn_run_strided(h, q, k, v, o, None, 0) == -1
     span_v = ((tokens - 1) * 3 * row + row) * 2
@@ -188,6 +189,15 @@ def test_run_strided_rejects_before_launch():
     assert run(q, k, v, q - ((tokens - 1) * row + row) * 2 + 16, fused) == -1  # o ends inside q's span
     assert run(0, k, v, o, fused) == -1
     sw.swin3d_wattn_destroy(h)
+
+
+def test_grid_extent_limit():
+    """Each grid extent must stay below 2^24 (the kernels' index arithmetic)."""
+    rc, h = _create(B=1, D=2, H=6, W=(1 << 24) - 12)
+    assert rc == 0
+    sw.swin3d_wattn_destroy(h)
+    assert _create(B=1, D=2, H=6, W=1 << 24)[0] == -2
+    assert _create(B=1, D=2, H=(1 << 24) + 6, W=12)[0] == -2
 
 
 def test_strerror():
