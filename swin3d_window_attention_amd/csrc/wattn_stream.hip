@@ -41,6 +41,14 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 // MFMA whose accumulator input comes from one of the last few MFMAs reads
 // its A/B registers late) and the order is pinned.
 #define ST_PIN_MFMA() __builtin_amdgcn_sched_barrier(0x7F6)
+// Instruction selection may still move a pure MFMA (one with a zero
+// accumulator in particular) away from its place, which the scheduling
+// barrier cannot undo. An empty volatile asm on the A operand before and on
+// the accumulator after each MFMA fixes the order: volatile asm statements
+// keep their source order, and each MFMA sits between two of them. They emit
+// no instruction.
+#define ST_BEFORE(a) asm volatile("" : "+v"(a))
+#define ST_AFTER(c) asm volatile("" : "+v"(c))
 
 constexpr uint32_t kPadSlot = 8;
 
@@ -162,7 +170,7 @@ __device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
 }
 
 template <int DH, int WAVES, int KC>
-__global__ __launch_bounds__(64 * WAVES) void wattn_stream_item(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 4 : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ o, const StreamParams p) {
@@ -305,7 +313,9 @@ __global__ __launch_bounds__(64 * WAVES) void wattn_stream_item(const uint16_t* 
         kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
+        ST_BEFORE(kf[kt]);
         S2[s % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[s], S2[s % kAcc][kt], 0, 0, 0);
+        ST_AFTER(S2[s % kAcc][kt]);
         ST_PIN_MFMA();
       }
     }
@@ -317,7 +327,9 @@ __global__ __launch_bounds__(64 * WAVES) void wattn_stream_item(const uint16_t* 
         xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
+        ST_BEFORE(xf[kt]);
         S2[kS % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S2[kS % kAcc][kt], 0, 0, 0);
+        ST_AFTER(S2[kS % kAcc][kt]);
         ST_PIN_MFMA();
       }
     }
@@ -404,14 +416,21 @@ __global__ __launch_bounds__(64 * WAVES) void wattn_stream_item(const uint16_t* 
     __syncthreads();
   }
 
-  // ---- normalise and scatter (queries of the window only) ----
+  // ---- normalise and scatter (queries of the window only): tiles 2 m and
+  // 2 m + 1 hold the two 8-byte halves of the 16-byte chunk at dims
+  // 32 m + 8 g4 (tile 2 m first for even g4, second for odd), one store each.
+  // (Staging the rows through LDS for whole-row stores measured slower
+  // here: the extra round trip sits at the end of every workgroup.) ----
   if (qcode != kPadSlot) {
     const float inv = 1.0f / l;
     uint16_t* out = o + (size_t)qtok * p.so + hoff;
+    const bool odd = g4 & 1;
 #pragma unroll
-    for (int t = 0; t < kT; ++t) {
-      const bf16x4_t w = __builtin_convertvector(O[t] * inv, bf16x4_t);
-      *reinterpret_cast<u32x2*>(out + dbase(t, g4)) = __builtin_bit_cast(u32x2, w);
+    for (int m2 = 0; m2 < kT / 2; ++m2) {
+      const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
+      const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2 + 1] * inv, bf16x4_t));
+      const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
+      *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
     }
   }
 }
