@@ -73,31 +73,49 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <typename XT, typename RT, typename OT>
+// U: 4-channel units per lane. U < kMaxUnits is exact (C = 256 U, the common
+// widths); U = kMaxUnits serves every other width, each unit guarded by
+// i < units. For U <= 4 every load of the row (x, res, gamma, beta) is issued
+// up front, so a wave makes one memory round trip before its stores; larger
+// rows load res, gamma and beta after the statistics to stay within the
+// register budget.
+template <typename XT, typename RT, typename OT, int U>
 __global__ __launch_bounds__(64 * kWaves) void adaln_residual_kernel(const XT* __restrict__ x, const RT* res,
                                                                       const float* __restrict__ gamma,
                                                                       const float* __restrict__ beta, OT* out,
                                                                       const AdalnParams p) {
+  constexpr bool kEarly = U <= 4;
+  constexpr bool kGuard = U == kMaxUnits;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= p.rows) return;  // whole waves only
   const int b = (int)fdiv((uint32_t)row, p.div_t);
   const size_t base = (size_t)row * p.C;
+  const float* g = gamma + (size_t)b * p.C;
+  const float* be = beta + (size_t)b * p.C;
 
-  floatx4 v[kMaxUnits];
+  floatx4 v[U], r[kEarly ? U : 1], gg[kEarly ? U : 1], bb[kEarly ? U : 1];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxUnits; ++i) {
-    if (i < p.units) {
-      v[i] = load4(x + base + 4 * (lane + 64 * i));
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  for (int i = 0; i < U; ++i) {
+    if (!kGuard || i < p.units) {
+      const int c = 4 * (lane + 64 * i);
+      v[i] = load4(x + base + c);
+      if constexpr (kEarly) {
+        r[i] = load4(res + base + c);
+        gg[i] = *reinterpret_cast<const floatx4*>(g + c);
+        bb[i] = *reinterpret_cast<const floatx4*>(be + c);
+      }
     }
   }
+#pragma unroll
+  for (int i = 0; i < U; ++i)
+    if (!kGuard || i < p.units) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
   const float mean = wave_sum(s) * p.inv_c;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxUnits; ++i) {
-    if (i < p.units) {
+  for (int i = 0; i < U; ++i) {
+    if (!kGuard || i < p.units) {
       const floatx4 d = v[i] - mean;
       v[i] = d;
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
@@ -105,22 +123,23 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_residual_kernel(const XT* _
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) * p.inv_c + p.eps);
 
-  const float* g = gamma + (size_t)b * p.C;
-  const float* be = beta + (size_t)b * p.C;
 #pragma unroll
-  for (int i = 0; i < kMaxUnits; ++i) {
-    if (i < p.units) {
+  for (int i = 0; i < U; ++i) {
+    if (!kGuard || i < p.units) {
       const int c = 4 * (lane + 64 * i);
-      const floatx4 gg = *reinterpret_cast<const floatx4*>(g + c);
-      const floatx4 bb = *reinterpret_cast<const floatx4*>(be + c);
-      const floatx4 r = load4(res + base + c);
-      store4(out + base + c, r + gg * (v[i] * rstd) + bb);
+      if constexpr (kEarly) {
+        store4(out + base + c, r[i] + gg[i] * (v[i] * rstd) + bb[i]);
+      } else {
+        const floatx4 g4 = *reinterpret_cast<const floatx4*>(g + c);
+        const floatx4 b4 = *reinterpret_cast<const floatx4*>(be + c);
+        store4(out + base + c, load4(res + base + c) + g4 * (v[i] * rstd) + b4);
+      }
     }
   }
 }
 
-template <typename XT, typename RT, typename OT>
-hipError_t launch_t(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+template <typename XT, typename RT, typename OT, int U>
+hipError_t launch_u(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
                     const float* beta, void* out, hipStream_t s) {
   AdalnParams p;
   p.rows = (int32_t)(d->rows * d->B);
@@ -134,8 +153,20 @@ hipError_t launch_t(const swin3d_adaln_desc_t* d, const void* x, const void* res
   OT* oo = static_cast<OT*>(out);
   void* args[] = {&xx, &rr, &gamma, &beta, &oo, &p};
   const unsigned blocks = (unsigned)((p.rows + kWaves - 1) / kWaves);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&adaln_residual_kernel<XT, RT, OT>), dim3(blocks),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&adaln_residual_kernel<XT, RT, OT, U>), dim3(blocks),
                          dim3(64 * kWaves), args, 0, s);
+}
+
+template <typename XT, typename RT, typename OT>
+hipError_t launch_t(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
+                    const float* beta, void* out, hipStream_t s) {
+  switch (d->C / 256) {  // 1..16, checked on the host
+    case 1: return launch_u<XT, RT, OT, 1>(d, x, res, gamma, beta, out, s);
+    case 2: return launch_u<XT, RT, OT, 2>(d, x, res, gamma, beta, out, s);
+    case 4: return launch_u<XT, RT, OT, 4>(d, x, res, gamma, beta, out, s);
+    case 8: return launch_u<XT, RT, OT, 8>(d, x, res, gamma, beta, out, s);
+    default: return launch_u<XT, RT, OT, kMaxUnits>(d, x, res, gamma, beta, out, s);
+  }
 }
 
 template <typename XT, typename RT>

@@ -34,6 +34,8 @@ CASES = [
     (2, 130, 1024, "bf16", "bf16", "bf16"),
     (1, 3, 4096, "f32", "bf16", "f32"),
     (1, 1, 768, "bf16", "f32", "bf16"),
+    (2, 65, 2048, "f32", "f32", "bf16"),     # 8 units per lane
+    (1, 9, 1792, "bf16", "bf16", "f32"),     # 7 units: the guarded kernel
 ]
 
 
