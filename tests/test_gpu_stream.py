@@ -27,6 +27,8 @@ SMALL = [
     wl_of("w4x12x24", 1, 4, 24, 48, 1, 64, (4, 12, 24), (2, 6, 12)),   # N = 1152: 18 chunks
     wl_of("w2x6x6_noshift", 1, 2, 12, 18, 2, 64, (2, 6, 6), (0, 0, 0)),  # no mask step but a partial chunk
     wl_of("single_token", 1, 1, 1, 1, 2, 128, (2, 6, 12), (1, 3, 6)),
+    wl_of("w3x12x12", 1, 6, 24, 24, 2, 128, (3, 12, 12), (1, 6, 6)),     # N = 432: 9 chunks of 48
+    wl_of("w16x16x16_max", 1, 16, 16, 20, 1, 64, (16, 16, 16), (8, 4, 10)),  # N = 4096, the largest window
 ]
 
 
