@@ -169,14 +169,14 @@ __device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(smem + byte_off));
 }
 
-template <int DH, int WAVES, int KC>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 4 : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
+template <int DH, int WAVES, int KC, int QT>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH == 64 ? (QT == 1 ? 4 : 3) : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ o, const StreamParams p) {
   using L = Lds<DH, KC>;
   constexpr int kThreads = 64 * WAVES;
-  constexpr int kQB = 16 * WAVES;                      // query slots per workgroup
+  constexpr int kQB = 16 * WAVES * QT;                 // query slots per workgroup (QT tiles per wave)
   constexpr int kKC = KC;                              // key slots per chunk
   constexpr int kKT = KC / 16;                         // key tiles per chunk
   constexpr int kJ = KC / 32;                          // whole 32-key steps of P V
@@ -206,16 +206,20 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
   const WinPos cur = decode_window(p, wq);
   const size_t hoff = (size_t)head * DH;
 
-  // ---- this wave's 16 queries: Q operands (lane (g4, query l16): dims
-  // 32 s + 8 g4 .. + 7), region code, token ----
-  const int qslot = qb * kQB + wave * 16 + l16;
-  int32_t qtok;
-  uint32_t qcode;
-  map_slot(p, cur, (uint32_t)qslot, qtok, qcode);
-  bf16x8_t qop[kS];
+  // ---- this wave's QT tiles of 16 queries (tile wave QT + u of the block):
+  // Q operands (lane (g4, query l16): dims 32 s + 8 g4 .. + 7), region code,
+  // token ----
+  int32_t qtok[QT];
+  uint32_t qcode[QT];
+  bf16x8_t qop[QT][kS];
 #pragma unroll
-  for (int s = 0; s < kS; ++s)
-    qop[s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok * p.sq + hoff + 32 * s + 8 * g4));
+  for (int u = 0; u < QT; ++u) {
+    const int qslot = qb * kQB + (wave * QT + u) * 16 + l16;
+    map_slot(p, cur, (uint32_t)qslot, qtok[u], qcode[u]);
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+      qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[u] * p.sq + hoff + 32 * s + 8 * g4));
+  }
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
   // (piece -> key row piece / kCh, chunk piece % kCh) ----
@@ -281,11 +285,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
   __syncthreads();
 
   const float c2 = p.c2;
-  float m = -INFINITY, l = 0.f;
-  floatx4 O[kT];
+  float m[QT], l[QT];
+  floatx4 O[QT][kT];
+  bf16x8_t qxb[QT];
 #pragma unroll
-  for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t qxb = *reinterpret_cast<const bf16x8_t*>(smem + L::kQt + (qcode * 4 + g4) * 16);
+  for (int u = 0; u < QT; ++u) {
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kT; ++t) O[u][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    qxb[u] = *reinterpret_cast<const bf16x8_t*>(smem + L::kQt + (qcode[u] * 4 + g4) * 16);
+  }
   const int e = l16 >> 2, qd = l16 & 3;
 
   for (int c = 0; c < p.nchunk; ++c) {
@@ -296,15 +306,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
     const bool more = c + 1 < p.nchunk;
     if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
 
-    // ---- S^T = K Q^T for this chunk's key tiles. With fewer than four key
-    // tiles, even and odd k-steps accumulate separately, so that no MFMA
-    // takes its accumulator from one of the three before it ----
-    constexpr int kAcc = kKT >= 4 ? 1 : 2;
-    floatx4 S2[kAcc][kKT];
+    // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
+    // for the wave's QT query tiles. Consecutive MFMAs take independent
+    // accumulators: with fewer than four per k-step, even and odd k-steps
+    // accumulate separately, so that no MFMA takes its accumulator from one
+    // of the three before it ----
+    constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
+    floatx4 S2[kAcc][QT][kKT];
 #pragma unroll
     for (int a = 0; a < kAcc; ++a)
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) S2[a][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) S2[a][u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
       bf16x8_t kf[kKT];
@@ -312,12 +326,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
       for (int kt = 0; kt < kKT; ++kt)
         kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        ST_BEFORE(kf[kt]);
-        S2[s % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[s], S2[s % kAcc][kt], 0, 0, 0);
-        ST_AFTER(S2[s % kAcc][kt]);
-        ST_PIN_MFMA();
-      }
+      for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          ST_BEFORE(kf[kt]);
+          S2[s % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[u][s], S2[s % kAcc][u][kt], 0, 0, 0);
+          ST_AFTER(S2[s % kAcc][u][kt]);
+          ST_PIN_MFMA();
+        }
     }
     // mask k-step: the window has a cut or padding, or this chunk runs past N
     if (cur.masked || (c + 1) * kKC > p.N) {
@@ -326,47 +342,54 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
       for (int kt = 0; kt < kKT; ++kt)
         xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        ST_BEFORE(xf[kt]);
-        S2[kS % kAcc][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb, S2[kS % kAcc][kt], 0, 0, 0);
-        ST_AFTER(S2[kS % kAcc][kt]);
-        ST_PIN_MFMA();
-      }
+      for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          ST_BEFORE(xf[kt]);
+          S2[kS % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb[u], S2[kS % kAcc][u][kt], 0, 0, 0);
+          ST_AFTER(S2[kS % kAcc][u][kt]);
+          ST_PIN_MFMA();
+        }
     }
-    floatx4 S[kKT];
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][kt] : S2[0][kt] + S2[kAcc - 1][kt];
 
-    // ---- online softmax ----
-    float mc = S[0][0];
+    // ---- online softmax, per query tile ----
+    bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
+    bf16x4_t Pt[QT];
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
+    for (int u = 0; u < QT; ++u) {
+      floatx4 S[kKT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, S[kt][i]);
-    const float m_new = fmaxf(m, wave_max16x4(mc));
-    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c2);  // 0 on the first chunk
-    const float nm = -m_new * c2;
-    floatx4 P[kKT];
-    float rs = 0.f;
+      for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
+      float mc = S[0][0];
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
-        rs += P[kt][i];
-      }
-    l = l * alpha + wave_sum16x4(rs);
-    m = m_new;
+        for (int i = 0; i < 4; ++i) mc = fmaxf(mc, S[kt][i]);
+      const float m_new = fmaxf(m[u], wave_max16x4(mc));
+      const float alpha = __builtin_amdgcn_exp2f((m[u] - m_new) * c2);  // 0 on the first chunk
+      const float nm = -m_new * c2;
+      floatx4 P[kKT];
+      float rs = 0.f;
 #pragma unroll
-    for (int t = 0; t < kT; ++t) O[t] *= alpha;
-    bf16x8_t Pb[kJ];
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-    for (int j = 0; j < kJ; ++j)
-      Pb[j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
-                                      __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x4_t Pt = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
+        for (int i = 0; i < 4; ++i) {
+          P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
+          rs += P[kt][i];
+        }
+      l[u] = l[u] * alpha + wave_sum16x4(rs);
+      m[u] = m_new;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
+                                           __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
+      Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
+    }
 
-    // ---- O^T += V^T P^T over the chunk's two 32-key steps ----
+    // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
+    // once for the wave's QT query tiles ----
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       u32x4 vf[kT];
@@ -380,10 +403,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
         vf[t] = u32x4{a[0], a[1], b[0], b[1]};
       }
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[j], O[t], 0, 0, 0);
-        ST_PIN_MFMA();
-      }
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
+          ST_PIN_MFMA();
+        }
     }
     if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
       short4_t vt[kT];
@@ -394,10 +419,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
         vt[t] = lds_tr(vb, key * (DH * 2) + (((d >> 3) ^ swz(key)) << 4) + ((d & 4) << 1));
       }
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
-        ST_PIN_MFMA();
-      }
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
+          ST_PIN_MFMA();
+        }
     }
 
     // ---- next chunk into the other buffer (everyone finished chunk c - 1,
@@ -421,24 +448,27 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
   // 32 m + 8 g4 (tile 2 m first for even g4, second for odd), one store each.
   // (Staging the rows through LDS for whole-row stores measured slower
   // here: the extra round trip sits at the end of every workgroup.) ----
-  if (qcode != kPadSlot) {
-    const float inv = 1.0f / l;
-    uint16_t* out = o + (size_t)qtok * p.so + hoff;
-    const bool odd = g4 & 1;
+  const bool odd = g4 & 1;
 #pragma unroll
-    for (int m2 = 0; m2 < kT / 2; ++m2) {
-      const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
-      const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2 + 1] * inv, bf16x4_t));
-      const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
-      *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
+  for (int u = 0; u < QT; ++u) {
+    if (qcode[u] != kPadSlot) {
+      const float inv = 1.0f / l[u];
+      uint16_t* out = o + (size_t)qtok[u] * p.so + hoff;
+#pragma unroll
+      for (int m2 = 0; m2 < kT / 2; ++m2) {
+        const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[u][2 * m2] * inv, bf16x4_t));
+        const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[u][2 * m2 + 1] * inv, bf16x4_t));
+        const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
+        *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
+      }
     }
   }
 }
 
-template <int DH, int WAVES, int KC>
+template <int DH, int WAVES, int KC, int QT>
 hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
                   const swin3d_wattn_strides_t* st, hipStream_t s) {
-  constexpr int kQB = 16 * WAVES;
+  constexpr int kQB = 16 * WAVES * QT;
   constexpr int kKC = KC;
   StreamParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
@@ -476,7 +506,7 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
   const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)d.heads);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC>), grid,
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT>), grid,
                          dim3(64 * WAVES), args, 0, s);
 }
 
@@ -487,9 +517,11 @@ int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool k48 = p->threads == 192;  // the plan's block shape: 3 waves and 48-key chunks
   hipError_t e;
+  // head_dim 64: two query tiles per wave (each K and V operand read from LDS
+  // serves both); head_dim 128: one, within the register budget
   if (p->desc.head_dim == 128)
-    e = k48 ? launch<128, 3, 48>(p, q, k, v, o, stride, s) : launch<128, 4, 64>(p, q, k, v, o, stride, s);
+    e = k48 ? launch<128, 3, 48, 1>(p, q, k, v, o, stride, s) : launch<128, 4, 64, 1>(p, q, k, v, o, stride, s);
   else
-    e = k48 ? launch<64, 3, 48>(p, q, k, v, o, stride, s) : launch<64, 4, 64>(p, q, k, v, o, stride, s);
+    e = k48 ? launch<64, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<64, 4, 64, 2>(p, q, k, v, o, stride, s);
   return (int)e;
 }
