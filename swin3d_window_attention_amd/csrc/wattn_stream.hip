@@ -7,8 +7,10 @@
 // shared memory. The N = 144, head_dim 64 production shape has its own
 // single-tile kernel; this one serves every other window and head_dim 128.
 //
-// Work: one workgroup per (window, head, block of query slots), 16 queries
-// per wave; K and V of the window pass through LDS in chunks of key slots,
+// Work: one workgroup per (window, head, block of query slots), QT tiles of
+// 16 queries per wave (two at head_dim 64, where each K and V operand read
+// from LDS serves both, one at head_dim 128); K and V of the window pass
+// through LDS in chunks of key slots,
 // double-buffered: while the waves work on chunk c, each thread holds its
 // part of chunk c + 1 in registers and writes it to the other buffer
 // afterwards (one barrier per chunk). Two block shapes: four waves and
