@@ -15,8 +15,9 @@
 // part of chunk c + 1 in registers and writes it to the other buffer
 // afterwards (one barrier per chunk). Two block shapes: four waves and
 // 64-key chunks, or, where the window size is a multiple of 48 but not of
-// 64 (144, 288, ...), three waves and 48-key chunks, so that no query or
-// key slot past the window is processed. Softmax is online in
+// 64 (144, 288, ...), three waves and 48-key chunks, so that no key slot
+// past the window is processed (nor a query slot, where N is a multiple of
+// the query block). Softmax is online in
 // FP32 (log2 domain): running max m and sum l per query, O rescaled by
 // 2^((m_old - m_new) c2) whenever the max grows.
 //
