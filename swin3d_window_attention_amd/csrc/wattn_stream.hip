@@ -62,7 +62,8 @@ struct Lds {
   static constexpr int kBuf = 2 * kTile + 64;        // K, V and the chunk's region codes
   static constexpr int kXt = 2 * kBuf;               // key feature table
   static constexpr int kQt = kXt + 9 * 4 * 16;       // query feature table
-  static constexpr int kBytes = kQt + 9 * 4 * 16;
+  static constexpr int kTok = kQt + 9 * 4 * 16;      // key tokens of two chunks (a ring)
+  static constexpr int kBytes = kTok + 2 * KC * 4;
 };
 
 struct FastDiv {
@@ -225,18 +226,33 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
   }
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
-  // (piece -> key row piece / kCh, chunk piece % kCh) ----
+  // (piece -> key row piece / kCh, chunk piece % kCh). Chunk 0 maps its own
+  // slots; every later chunk's key tokens were mapped once per slot, two
+  // chunks ahead, into a two-entry ring in LDS (entry c & 1 for chunk c) ----
   u32x4 kr[kLoads], vr[kLoads];
+  int32_t* tok_ring = reinterpret_cast<int32_t*>(smem + L::kTok);
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int piece = tid + kThreads * i;
       int32_t t;
-      uint32_t unused;
-      map_slot(p, cur, (uint32_t)(c * kKC + piece / kCh), t, unused);
+      if (c == 0) {
+        uint32_t unused;
+        map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
+      } else {
+        t = tok_ring[(c & 1) * kKC + piece / kCh];
+      }
       kr[i] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
       vr[i] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
     }
+  };
+  // token of key slot r of chunk c into the ring, its region code returned
+  auto map_ahead = [&](int c, int r) {
+    int32_t t;
+    uint32_t code;
+    map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
+    tok_ring[(c & 1) * kKC + r] = t;
+    return code;
   };
 
   // mask-feature tables: also unmasked windows use them when the last chunk
@@ -285,6 +301,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
     *reinterpret_cast<u32x4*>(smem + L::kTile + row_off<DH>(r, c)) = vr[i];
   }
   if (tid < kKC) smem[2 * L::kTile + tid] = (uint8_t)code_of(0, tid);
+  // chunk 1 ahead: its tokens into the ring, its codes kept for staging
+  uint32_t next_code = 0;
+  if (tid < kKC && p.nchunk > 1) next_code = map_ahead(1, tid);
   __syncthreads();
 
   const float c2 = p.c2;
@@ -308,6 +327,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
     const uint8_t* cb = kb + 2 * L::kTile;
     const bool more = c + 1 < p.nchunk;
     if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
+    // chunk c + 2 ahead, into ring entry c & 1 (chunk c's tokens, last read
+    // by the loads of the previous iteration, before its barrier)
+    uint32_t code2 = 0;
+    if (tid < kKC && c + 2 < p.nchunk) code2 = map_ahead(c + 2, tid);
 
     // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
     // for the wave's QT query tiles. Consecutive MFMAs take independent
@@ -441,8 +464,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
         *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, cc)) = kr[i];
         *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, cc)) = vr[i];
       }
-      if (tid < kKC) nb[2 * L::kTile + tid] = (uint8_t)code_of(c + 1, tid);
+      if (tid < kKC) nb[2 * L::kTile + tid] = (uint8_t)next_code;
     }
+    next_code = code2;
     __syncthreads();
   }
 
