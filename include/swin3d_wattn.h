@@ -123,7 +123,8 @@ typedef struct {
 
 /* swin3d_wattn_run with explicit token strides (see swin3d_wattn_strides_t).
  * Each stride must be >= heads*head_dim, below 2^31 elements and a multiple
- * of 16 bytes; the pointers 16-byte aligned. The span of a tensor is the byte range
+ * of 16 bytes, and each span (below) at most 2^46 elements; the pointers
+ * 16-byte aligned. The span of a tensor is the byte range
  * [ptr, ptr + ((tokens - 1) * stride + heads*head_dim) * element size); the
  * span of O must not overlap the spans of Q, K or V, while Q, K and V may
  * overlap each other. Elements of

@@ -222,9 +222,10 @@ extern "C" int swin3d_wattn_get_info(swin3d_wattn_t plan, swin3d_wattn_info_t* i
 }
 
 namespace {
+// byte ranges [a, a + a_bytes) and [b, b + b_bytes) intersect (128-bit sums: no wrap-around)
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
-  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
+  const unsigned __int128 x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (unsigned __int128)b_bytes && y < x + (unsigned __int128)a_bytes;
 }
 bool misaligned(const void* a) { return ((uintptr_t)a & 15u) != 0; }
 }  // namespace
@@ -238,7 +239,9 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
   int64_t span[4];
   for (int i = 0; i < 4; ++i) {
     if (s[i] < row || s[i] >= (int64_t(1) << 31) || (s[i] * plan->elem_bytes) % 16 != 0) return SWIN3D_WATTN_EINVAL;
-    span[i] = ((plan->tokens - 1) * s[i] + row) * plan->elem_bytes;
+    const int64_t elems = (plan->tokens - 1) * s[i] + row;  // < 2^62: tokens and stride are < 2^31
+    if (elems > (int64_t(1) << 46)) return SWIN3D_WATTN_EINVAL;  // no device holds such a span
+    span[i] = elems * plan->elem_bytes;
   }
   if (overlaps(o, span[3], q, span[0]) || overlaps(o, span[3], k, span[1]) || overlaps(o, span[3], v, span[2]))
     return SWIN3D_WATTN_EINVAL;
@@ -267,7 +270,7 @@ extern "C" int swin3d_adaln_residual(const swin3d_adaln_desc_t* d, const void* x
   if (d->rows <= 0 || d->B <= 0 || d->C <= 0) return SWIN3D_WATTN_EINVAL;
   if (!std::isfinite(d->eps) || !(d->eps > 0.0f)) return SWIN3D_WATTN_EINVAL;
   if (d->C % 256 != 0 || d->C > 4096) return SWIN3D_WATTN_EUNSUPPORTED;
-  if (d->rows * (int64_t)d->B >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
+  if (d->rows >= (int64_t(1) << 31) || d->rows * (int64_t)d->B >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
   const int64_t n = d->rows * d->B * d->C;
   auto bytes = [n](int32_t t) { return n * (t == SWIN3D_WATTN_BF16 ? 2 : 4); };
   const int64_t xb = bytes(d->x_dtype), rb = bytes(d->res_dtype), ob = bytes(d->out_dtype);

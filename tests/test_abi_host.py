@@ -192,6 +192,19 @@ def test_run_strided_rejects_before_launch():
     sw.swin3d_wattn_destroy(h)
 
 
+def test_run_strided_rejects_oversized_span():
+    """A span beyond 2^46 elements is refused before any arithmetic on it could overflow."""
+    rc, h = _create(B=1, D=1024, H=1024, W=1020, heads=1, head_dim=64, window=(2, 6, 12), shift=(1, 3, 6))
+    assert rc == 0                                          # 2^30 - 4 Mi tokens
+    S = sw.Swin3dWattnStrides
+    base = 1 << 44
+    big = (1 << 31) - 8                                     # allowed stride, span ~2^61 elements
+    run = lambda st: sw.swin3d_wattn_run_strided(h, base, base, base, base + (1 << 47), st, 0)
+    assert run(S(64, 64, 64, big)) == -1
+    assert run(S(big, 64, 64, 64)) == -1
+    sw.swin3d_wattn_destroy(h)
+
+
 def test_grid_extent_limit():
     """Each grid extent must stay below 2^24 (the kernels' index arithmetic)."""
     rc, h = _create(B=1, D=2, H=6, W=(1 << 24) - 12)
@@ -224,6 +237,7 @@ def test_adaln_rejects_before_launch():
     assert run(D(0, 2, 512, 1, 0, 0, 1e-5), x, res, g, b, out) == -1
     assert run(D(100, 2, 512, 2, 0, 0, 1e-5), x, res, g, b, out) == -1    # no split dtype here
     assert run(D(1 << 30, 4, 256, 1, 0, 0, 1e-5), x, res, g, b, out) == -2  # too many rows
+    assert run(D(1 << 62, 4, 256, 1, 0, 0, 1e-5), x, res, g, b, out) == -2  # rows * B would overflow
     assert run(ok, 0, res, g, b, out) == -1
     assert run(ok, x + 8, res, g, b, out) == -1                            # misaligned
     assert run(ok, x, res, g, b, x + 16) == -1                             # out overlaps x
