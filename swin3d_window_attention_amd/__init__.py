@@ -239,19 +239,24 @@ class Plan:
             if _dtype_code(t.dtype) != _io_code(self.desc.dtype):
                 raise ValueError("tensor dtype does not match the plan")
             strides.append(self._token_stride(t))
+        if any(t.device != q.device for t in (k, v, o)):
+            raise ValueError("q, k, v, o must be on one device")
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         elif isinstance(stream, torch.cuda.Stream):
+            if stream.device != q.device:
+                raise ValueError("the stream must belong to the tensors' device")
             stream = stream.cuda_stream
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
         row = self.shape[4] * self.shape[5]
-        if all(s == row for s in strides):
-            rc = self._lib.swin3d_wattn_run(self._h, *ptrs, stream)
-            where = "swin3d_wattn_run"
-        else:
-            rc = self._lib.swin3d_wattn_run_strided(self._h, *ptrs, ctypes.byref(Swin3dWattnStrides(*strides)),
-                                                    stream)
-            where = "swin3d_wattn_run_strided"
+        with torch.cuda.device(q.device):  # the launch goes to the current device
+            if all(s == row for s in strides):
+                rc = self._lib.swin3d_wattn_run(self._h, *ptrs, stream)
+                where = "swin3d_wattn_run"
+            else:
+                rc = self._lib.swin3d_wattn_run_strided(self._h, *ptrs,
+                                                        ctypes.byref(Swin3dWattnStrides(*strides)), stream)
+                where = "swin3d_wattn_run_strided"
         if rc != SWIN3D_WATTN_OK:
             raise Swin3dWattnError(rc, where)
 
@@ -296,16 +301,21 @@ def adaln_residual(x, res, gamma, beta, eps=1e-5, out=None, out_dtype=None, stre
         raise ValueError("gamma and beta must be float32")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or res.dtype, device=x.device)
-    if out.shape != x.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, rows, C] tensor")
+    if out.shape != x.shape or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous [B, rows, C] device tensor")
+    if any(t.device != x.device for t in (res, gamma, beta, out)):
+        raise ValueError("x, res, gamma, beta, out must be on one device")
     d = Swin3dAdalnDesc(x.shape[1], x.shape[0], x.shape[2], _dtype_code(x.dtype), _dtype_code(res.dtype),
                         _dtype_code(out.dtype), eps)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     elif isinstance(stream, torch.cuda.Stream):
+        if stream.device != x.device:
+            raise ValueError("the stream must belong to the tensors' device")
         stream = stream.cuda_stream
-    rc = swin3d_adaln_residual(d, x.data_ptr(), res.data_ptr(), gamma.data_ptr(), beta.data_ptr(),
-                               out.data_ptr(), stream)
+    with torch.cuda.device(x.device):  # the launch goes to the current device
+        rc = swin3d_adaln_residual(d, x.data_ptr(), res.data_ptr(), gamma.data_ptr(), beta.data_ptr(),
+                                   out.data_ptr(), stream)
     if rc != SWIN3D_WATTN_OK:
         raise Swin3dWattnError(rc, "swin3d_adaln_residual")
     return out
