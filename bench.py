@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "window-attention tokens/s at 0.25° stage-1 shape; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 (matrix)
 KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "wattn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wattn_bf16_stage1.json")
 
@@ -225,6 +226,7 @@ def main():
                     help="stage1 (default, the headline line) or another workload: stage2, stage2_s0, "
                          "stage3_pad, stress_hres (bf16), stage1_f32_split, stage3_pad_f32_split, "
                          "stress_f32_split (FP32 I/O on the split-bf16 matrix-core kernel), "
+                         "stage1_f32, stage3_pad_f32, stress_f32 (exact FP32 on the matrix cores), "
                          "adaln_stage1 (the fused AdaLN + residual step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -261,7 +263,7 @@ def main():
     import swin3d_window_attention_amd as sw
 
     wl = datagen.WORKLOADS[args.workload]
-    if wl.plan_dtype not in ("bf16", "f32_split"):
+    if wl.plan_dtype not in ("bf16", "f32_split", "f32"):
         sys.exit(f"bench.py: workload {wl.name} is a {wl.dtype} parity case, not a benchmark")
     headline = wl.name == "stage1"
     dev = torch.device("cuda:0")
@@ -322,7 +324,10 @@ def main():
     gbs = nbytes / sec / 1e9
     tflops = flops / sec / 1e12
     frac_hbm = gbs / HBM_PEAK_GBS
-    frac_mfma = tflops / BF16_MFMA_PEAK_TFLOPS
+    # the matrix-core peak of the products' own type (exact FP32 runs FP32 MFMAs)
+    mfma_peak = F32_MFMA_PEAK_TFLOPS if wl.plan_dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    frac_mfma = tflops / mfma_peak
+    mfma_bound = flops / (mfma_peak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
 
     cpu = None
     if not args.no_cpu_baseline and headline:
@@ -340,7 +345,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32 I/O, bf16x3 split products, f32 softmax",
+        "dtype": ("bf16" if wl.dtype == "bf16"
+                  else "f32 I/O, bf16x3 split products, f32 softmax" if wl.plan_dtype == "f32_split"
+                  else "f32"),
         "data": ("synthetic (seeded iid N(0,1) rounded to bf16)" if wl.dtype == "bf16"
                  else "synthetic (seeded iid float32 draws)"),
         "config": {
@@ -352,15 +359,22 @@ def main():
             "cache": ("flushed (1 GiB read) before each launch" if args.cold
                       else "warm (back-to-back launches)"),
         },
-        "roofline": {
+        "roofline": ({
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": mfma_peak,
+            "unit": "TFLOP/s",
+            "frac": frac_mfma,
+            "traffic": None,
+        } if mfma_bound else {
             "bound": "hbm",
             "achieved": gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": frac_hbm,
             "traffic": measured_traffic() if headline else None,
-        },
-        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": frac_mfma},
+        }),
+        "mfma": {"achieved_tflops": tflops, "peak_tflops": mfma_peak, "frac": frac_mfma},
         "algorithmic_bytes_per_launch": nbytes,
         "algorithmic_flops_per_launch": flops,
         "cpu_baseline": cpu,

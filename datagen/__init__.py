@@ -94,6 +94,11 @@ WORKLOADS = {
                                      "f32", 3, plan="f32_split"),
     "stress_f32_split": Workload("stress_f32_split", 1, 4, 90, 180, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 4,
                                  qk_mult=8.0, v_dist="uniform", plan="f32_split"),
+    # the same shapes on the exact FP32 path (FP32 matrix-core products)
+    "stage1_f32": Workload("stage1_f32", 1, 4, 180, 360, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 1),
+    "stage3_pad_f32": Workload("stage3_pad_f32", 1, 4, 45, 90, 32, 64, (2, 6, 12), (1, 3, 6), "f32", 3),
+    "stress_f32": Workload("stress_f32", 1, 4, 90, 180, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 4,
+                           qk_mult=8.0, v_dist="uniform"),
 }
 
 

@@ -29,7 +29,8 @@
  * Precision: bf16 I/O uses bf16 matrix-core products for Q K^T and P V with
  * FP32 accumulation and an FP32 softmax; P is rounded to bf16 (nearest-even)
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
- * computes everything in FP32. The bf16 kernel fills the padding slots of a
+ * computes everything in FP32 (FP32 matrix-core products for 144-slot
+ * windows, the vector ALU for other windows). The bf16 kernel fills the padding slots of a
  * window with the nearest real token and gives them a zero weight, so Q, K
  * and V must be finite: an Inf or NaN there may also reach the windows that
  * border the padding.
@@ -90,7 +91,9 @@ typedef struct swin3d_wattn_plan* swin3d_wattn_t;
  * single-tile kernel; every other case streams K and V through LDS in
  * 48- or 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with
  * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
- * or 64 and wd*wh*ww <= 256. B*D*H*W must be < 2^31 and each of D, H, W < 2^24.
+ * or 64 and wd*wh*ww <= 256 (wd*wh*ww = 144 with heads < 65536 on the matrix
+ * cores, other windows on the vector ALU). B*D*H*W must be < 2^31 and each
+ * of D, H, W < 2^24.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
 int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
@@ -183,7 +186,8 @@ typedef struct {
   int32_t threads_per_workgroup;
   int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel,
                                2 = f32 split-bf16 matrix-core kernel, 3 = bf16 matrix-core
-                               kernel with K/V streamed through LDS */
+                               kernel with K/V streamed through LDS, 4 = f32 matrix-core
+                               kernel */
 } swin3d_wattn_info_t;
 
 /* Fill *info for a plan. Host-only. Returns 0 or EINVAL. */

@@ -99,7 +99,10 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
       threads = (N % 64 != 0 && N % 48 == 0) ? 192 : 256;
     }
   } else {
-    if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
+    if ((d.head_dim == 32 || d.head_dim == 64) && N == 144 && d.heads < 65536) {
+      kernel = 4;  // FP32 on the matrix cores
+      threads = 256;
+    } else if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
       kernel = 0;
       threads = (int32_t)(ceil_div(N, 64) * 64);
     }
@@ -248,6 +251,7 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
   const int e = plan->kernel == 1   ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
                 : plan->kernel == 2 ? wattn_launch_f32x3(plan, q, k, v, o, st, stream)
                 : plan->kernel == 3 ? wattn_launch_stream(plan, q, k, v, o, st, stream)
+                : plan->kernel == 4 ? wattn_launch_f32m(plan, q, k, v, o, st, stream)
                                     : wattn_launch_f32(plan, q, k, v, o, st, stream);
   return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }

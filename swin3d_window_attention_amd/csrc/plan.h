@@ -15,7 +15,8 @@ struct swin3d_wattn_plan {
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
   int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA (N = 144, dh 64), 2: f32 split-bf16 MFMA,
-                            // 3: bf16 MFMA with K/V streamed (any N, dh 64 or 128)
+                            // 3: bf16 MFMA with K/V streamed (any N, dh 64 or 128),
+                            // 4: f32 MFMA (N = 144, dh 32 or 64)
   int64_t workgroups;       // workgroups one run launches
   int32_t threads;          // threads per workgroup
   float c2;                 // scale * log2(e)
@@ -42,6 +43,8 @@ int wattn_launch_f32x3(const swin3d_wattn_plan* p, const void* q, const void* k,
                        const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                         const swin3d_wattn_strides_t* stride, void* stream);
+int wattn_launch_f32m(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                      const swin3d_wattn_strides_t* stride, void* stream);
 // adaln.hip: the fused AdaLN + residual kernel for an already validated desc.
 int adaln_launch(const swin3d_adaln_desc_t* d, const void* x, const void* res, const float* gamma,
                  const float* beta, void* out, void* stream);

@@ -1,0 +1,391 @@
+// Swin3D shifted-window attention, exact FP32 on the matrix cores, for gfx950
+// (MI355X): windows of N = 144 slots, head_dim 32 or 64.
+//
+// This is the FP32 path of the method at matrix-core speed: both products
+// run on v_mfma_f32_16x16x4_f32 (FP32 operands, FP32 accumulation, no
+// reduced-precision step anywhere), and the shifted-window mask, the
+// softmax and P stay in FP32 on the vector ALU. The Flash-Aurora README
+// ("Window attention kernels", "CuTe DSL window attention") keeps the whole
+// window's K and V in one shared-memory tile; so does this kernel.
+//
+// Work: one workgroup of four waves per (window, head), head-major launch
+// grid (window, head); the nine 16-query tiles of a window are dealt to the
+// waves with a rotation by workgroup, so the wave that takes three tiles
+// does not always sit on the same SIMD. Index map for pad / cyclic shift /
+// partition and the scatter back to grid layout as in the other kernels
+// ("Kernel fusion for backbone memory traffic").
+//
+// Layouts (16x16x4 FP32 MFMA: lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the result D[4 (l / 16) + i][l % 16], i = 0..3):
+//  S^T = K Q^T: A = 16 keys x 4 dims of K, B = 4 dims x 16 queries of Q^T.
+//    The contraction order over dims is free, so k-step s of lane group kk
+//    takes dim kk DH/4 + s: a lane's K and Q values are contiguous and come
+//    four at a time (16-byte loads). K is row-major in LDS, 16-byte chunks
+//    XOR-swizzled by row, so these reads are conflict-free.
+//  O^T = V^T P^T: the S^T accumulator gives lane (g4, query) keys
+//    16 kt + 4 g4 + i, which is the B operand of k-step (kt, i) with
+//    key(kk) = 16 kt + 4 kk + i; P never leaves registers. The A operand
+//    (dims x those keys) is read from V stored transposed in LDS (rows of
+//    144 keys, padded to 148 floats so the 16 rows of a read hit distinct
+//    banks): lane (kk, dim m) gets keys 16 kt + 4 kk .. + 3, the operands of
+//    four consecutive k-steps, in one 16-byte read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "plan.h"
+
+namespace {
+
+typedef float floatx4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+
+// Matrix-core ordering: consecutive MFMAs use independent accumulators (an
+// MFMA whose accumulator input comes from one of the last few MFMAs reads
+// its A/B registers late). The scheduling barrier pins the MFMA order; the
+// empty volatile asm statements around each MFMA (on its A operand before,
+// on its accumulator after) also stop instruction selection from moving a
+// pure MFMA, which the barrier cannot undo. They emit no instruction.
+#define FM_PIN_MFMA() __builtin_amdgcn_sched_barrier(0x7F6)
+#define FM_BEFORE(a) asm volatile("" : "+v"(a))
+#define FM_AFTER(c) asm volatile("" : "+v"(c))
+
+constexpr int kN = 144;
+constexpr int kNT = 9;  // key / query tiles of 16
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kPadSlot = 8;  // region code of a padding slot
+constexpr int kVtPitch = 148;     // floats per transposed-V row (144 keys + 4)
+
+template <int DH>
+struct Lds {
+  static constexpr int kK = 0;                       // K, row-major, 144 x DH floats
+  static constexpr int kVt = kN * DH * 4;            // V^T, DH x 148 floats
+  static constexpr int kCode = kVt + DH * kVtPitch * 4;
+  static constexpr int kTok = kCode + kN;            // 4-byte aligned: kN is a multiple of 4
+  static constexpr int kBytes = kTok + kN * 4;
+};
+
+// floor(n / d) for 0 <= n < 2^31 as (n * mul) >> shr with shr = 31 + ceil(log2 d)
+// and mul = ceil(2^shr / d) (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
+struct FastDiv {
+  uint32_t mul, shr;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint32_t shr = 31 + l;
+  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
+}
+
+struct AttnParams {
+  int32_t X[3], P[3], shift[3], win[3], nwin[3];
+  int32_t special[3][3];
+  FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
+  FastDiv div_hw, div_w;        // by window slots per depth step, per row
+  int64_t sq, sk, sv, so;       // token strides of Q, K, V, O (elements)
+  float c2;                     // scale * log2(e)
+  float bias_s;                 // cross-region bias / scale (may be -inf)
+};
+
+__device__ __forceinline__ float wave_max16x4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum16x4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+struct WinPos {
+  int b, k[3];
+  bool masked;
+};
+
+__device__ __forceinline__ WinPos decode_window(const AttnParams& p, uint32_t w) {
+  WinPos it;
+  const uint32_t per_d = (uint32_t)(p.nwin[1] * p.nwin[2]);
+  it.b = (int)fdiv(w, p.div_b);
+  w -= (uint32_t)it.b * per_d * (uint32_t)p.nwin[0];
+  it.k[0] = (int)fdiv(w, p.div_d);
+  w -= (uint32_t)it.k[0] * per_d;
+  it.k[1] = (int)fdiv(w, p.div_h);
+  it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
+  bool m = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
+  it.masked = m;
+  return it;
+}
+
+// Slot n = (od, oh, ow) of the window -> token (padding: the nearest real
+// token, a stand-in whose key weight is 0 and whose query is not written)
+// and region code (one bit per shifted axis: position in [P - s, P)), or
+// kPadSlot for padding.
+__device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, uint32_t n, int32_t& tok,
+                                         uint32_t& code) {
+  int o[3];
+  o[0] = (int)fdiv(n, p.div_hw);
+  const uint32_t r = n - (uint32_t)o[0] * (uint32_t)(p.win[1] * p.win[2]);
+  o[1] = (int)fdiv(r, p.div_w);
+  o[2] = (int)(r - (uint32_t)o[1] * (uint32_t)p.win[2]);
+  int g[3];
+  uint32_t c = 0;
+  bool valid = true;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int pa = it.k[a] * p.win[a] + o[a];
+    int ga = pa + p.shift[a];
+    ga = ga >= p.P[a] ? ga - p.P[a] : ga;
+    valid = valid && ga < p.X[a];
+    g[a] = min(ga, p.X[a] - 1);
+    c |= pa >= p.P[a] - p.shift[a] ? (1u << a) : 0u;
+  }
+  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
+  code = valid ? c : kPadSlot;
+}
+
+// Q, K, V are read once: non-temporal loads
+__device__ __forceinline__ u32x4 ldg16(const float* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
+// byte offset of 16-byte chunk c of K row r (DH / 4 chunks per row, XOR-swizzled by row)
+template <int DH>
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * (DH * 4) + ((c ^ (r & (DH / 4 - 1))) << 4);
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wattn_f32m_item(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
+    const AttnParams p) {
+  using L = Lds<DH>;
+  constexpr int kCh = DH / 4;                 // 16-byte chunks per row
+  constexpr int kQC = DH / 16;                // 16-byte chunks of a lane's dims (= k-step groups of 4)
+  constexpr int kT = DH / 16;                 // 16-dim output tiles
+  constexpr int kAccP = kT >= 4 ? 1 : 2;      // P V accumulator sets (independent neighbours)
+  constexpr int kChunks = kN * kCh;
+  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
+  constexpr int kMaxQT = (kNT + kWaves - 1) / kWaves;
+  __shared__ __align__(16) uint8_t smem[L::kBytes];
+  uint8_t* codeS = smem + L::kCode;
+  int32_t* tokS = reinterpret_cast<int32_t*>(smem + L::kTok);
+  float* vt = reinterpret_cast<float*>(smem + L::kVt);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const int head = blockIdx.y;
+  const WinPos cur = decode_window(p, blockIdx.x);
+  const size_t hoff = (size_t)head * DH;
+  // query tiles of this wave: (wave - rot) mod 4 + 4 i; the rotation moves
+  // the three-tile share from wave to wave across workgroups
+  const int rot = (int)((blockIdx.x + blockIdx.y) & 3u);
+  const int first = (wave - rot) & 3;
+
+  // ---- gather: K and V rows whole (kCh lanes x 16 B per row), each thread
+  // mapping the slots it loads; Q straight into the B-operand layout ----
+  u32x4 kr[kPer], vr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < kChunks) {
+      int32_t t;
+      uint32_t unused;
+      map_slot(p, cur, (uint32_t)(c / kCh), t, unused);
+      kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c % kCh));
+      vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
+    }
+  }
+  // lane (kk = g4, query l16) of a tile holds dims kk DH/4 .. + DH/4 - 1
+  floatx4 qf[kMaxQT][kQC];
+#pragma unroll
+  for (int qi = 0; qi < kMaxQT; ++qi) {
+    const int qt = first + kWaves * qi;
+    if (qt < kNT) {
+      int32_t t;
+      uint32_t unused;
+      map_slot(p, cur, (uint32_t)(qt * 16 + l16), t, unused);
+      const float* base = q + (size_t)t * p.sq + hoff + g4 * (DH / 4);
+#pragma unroll
+      for (int c = 0; c < kQC; ++c) qf[qi][c] = __builtin_bit_cast(floatx4, ldg16(base + 4 * c));
+    }
+  }
+  // ---- K row-major (swizzled), V transposed into LDS ----
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < kChunks) {
+      const int r = c / kCh, ch = c % kCh;
+      *reinterpret_cast<u32x4*>(smem + L::kK + k_off<DH>(r, ch)) = kr[j];
+      const floatx4 x = __builtin_bit_cast(floatx4, vr[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[(4 * ch + e) * kVtPitch + r] = x[e];
+    }
+  }
+  // ---- slot table (token, region code) for the mask and the scatter ----
+  for (int r = tid; r < kN; r += kThreads) {
+    int32_t t;
+    uint32_t c;
+    map_slot(p, cur, (uint32_t)r, t, c);
+    tokS[r] = t;
+    codeS[r] = (uint8_t)c;
+  }
+  __syncthreads();
+
+  const float c2 = p.c2, bias_s = p.bias_s;
+#pragma unroll
+  for (int qi = 0; qi < kMaxQT; ++qi) {
+    const int qt = first + kWaves * qi;
+    if (qt >= kNT) break;
+
+    // ---- S^T = K Q^T: k-step s = 4 c + e of lane group kk is dim kk DH/4 + s ----
+    floatx4 S[kNT];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+      floatx4 kf[kNT];
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt)
+        kf[kt] = *reinterpret_cast<const floatx4*>(smem + L::kK + k_off<DH>(kt * 16 + l16, g4 * kQC + c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int kt = 0; kt < kNT; ++kt) {
+          float a = kf[kt][e];
+          FM_BEFORE(a);
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[qi][c][e], S[kt], 0, 0, 0);
+          FM_AFTER(S[kt]);
+          FM_PIN_MFMA();
+        }
+    }
+
+    // ---- shifted-window bias (bias / scale) and padding exclusion, added in
+    // the units of Q K^T; a padding query (never written) takes no bias. The
+    // row max is subtracted before scaling, so the largest weights see no
+    // rounding of a large scaled logit: p = 2^((s - max) scale log2(e)) ----
+    const uint32_t qc = codeS[qt * 16 + l16];
+    if (cur.masked) {
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) {
+        const uint32_t kc4 = *reinterpret_cast<const uint32_t*>(codeS + kt * 16 + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t kc = (kc4 >> (8 * i)) & 0xFFu;
+          const float add = kc == kPadSlot ? -INFINITY : (qc != kPadSlot && kc != qc ? bias_s : 0.f);
+          S[kt][i] += add;
+        }
+      }
+    }
+    float mx = S[0][0];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
+    mx = wave_max16x4(mx);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        S[kt][i] = __builtin_amdgcn_exp2f((S[kt][i] - mx) * c2);  // P, FP32
+        rs += S[kt][i];
+      }
+    const float inv = 1.0f / wave_sum16x4(rs);
+
+    // ---- O^T = V^T P^T: k-step (kt, i) covers keys 16 kt + 4 kk + i ----
+    floatx4 O[kAccP][kT];
+#pragma unroll
+    for (int a = 0; a < kAccP; ++a)
+#pragma unroll
+      for (int t = 0; t < kT; ++t) O[a][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) {
+      floatx4 va[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+        va[t] = *reinterpret_cast<const floatx4*>(vt + (16 * t + l16) * kVtPitch + 16 * kt + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          float a = va[t][i];
+          FM_BEFORE(a);
+          O[i % kAccP][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S[kt][i], O[i % kAccP][t], 0, 0, 0);
+          FM_AFTER(O[i % kAccP][t]);
+          FM_PIN_MFMA();
+        }
+    }
+
+    // ---- normalise and scatter: tile t holds dims 16 t + 4 g4 .. + 3 of query l16 ----
+    if (qc != kPadSlot) {
+      float* out = o + (size_t)tokS[qt * 16 + l16] * p.so + hoff + 4 * g4;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        const floatx4 r = kAccP == 1 ? O[0][t] : O[0][t] + O[kAccP - 1][t];
+        *reinterpret_cast<floatx4*>(out + 16 * t) = r * inv;
+      }
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+                  const swin3d_wattn_strides_t* st, hipStream_t s) {
+  AttnParams p;
+  const swin3d_wattn_desc_t& d = pl->desc;
+  p.X[0] = d.D;
+  p.X[1] = d.H;
+  p.X[2] = d.W;
+  for (int a = 0; a < 3; ++a) {
+    p.P[a] = pl->padded[a];
+    p.shift[a] = d.shift[a];
+    p.win[a] = d.window[a];
+    p.nwin[a] = pl->nwin[a];
+    for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
+  }
+  p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
+  p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
+  p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
+  p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
+  p.div_w = make_fastdiv((uint32_t)d.window[2]);
+  p.sq = st->q;
+  p.sk = st->k;
+  p.sv = st->v;
+  p.so = st->o;
+  p.c2 = pl->c2;
+  p.bias_s = std::isinf(d.cross_region_bias) ? -INFINITY
+                                             : (float)((double)d.cross_region_bias / (double)d.scale);
+  const float* qq = static_cast<const float*>(q);
+  const float* kk = static_cast<const float*>(k);
+  const float* vv = static_cast<const float*>(v);
+  float* oo = static_cast<float*>(o);
+  void* args[] = {&qq, &kk, &vv, &oo, &p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_f32m_item<DH>),
+                         dim3((unsigned)pl->n_windows, (unsigned)d.heads), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace
+
+int wattn_launch_f32m(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                      const swin3d_wattn_strides_t* stride, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = p->desc.head_dim == 32 ? launch<32>(p, q, k, v, o, stride, s)
+                                              : launch<64>(p, q, k, v, o, stride, s);
+  return (int)e;
+}

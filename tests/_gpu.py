@@ -11,7 +11,7 @@ import datagen
 import oracle
 import swin3d_window_attention_amd as sw
 
-from _tolerances import BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, SPLIT_TOL  # noqa: F401
+from _tolerances import BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_TOL, SPLIT_TOL  # noqa: F401
 
 
 def say(msg: str) -> None:
@@ -61,7 +61,9 @@ def check(wl: datagen.Workload, got: np.ndarray, ref: np.ndarray, what: str = ""
         assert max_abs <= tol_abs, (wl.name, what, max_abs)
         assert rel <= tol_rel, (wl.name, what, rel)
     elif wl.dtype == "f32":
-        assert max_abs <= F32_MAX_ABS, (wl.name, what, max_abs)
+        tol_abs, tol_rel = F32_TOL[wl.qk_mult]
+        assert max_abs <= tol_abs, (wl.name, what, max_abs)
+        assert rel <= tol_rel, (wl.name, what, rel)
     else:
         assert max_abs <= BF16_MAX_ABS, (wl.name, what, max_abs)
         assert rel <= BF16_REL_L2, (wl.name, what, rel)

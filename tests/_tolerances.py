@@ -1,6 +1,11 @@
 """Acceptance bars of the GPU parity tests against the fp64 oracle, over real tokens."""
 
 F32_MAX_ABS = 1e-5
+# FP32 I/O on exact FP32 arithmetic, by data class (qk_mult -> (max abs, rel L2)): the FP32 bar
+# on N(0,1) data; with Q, K scaled by 8 about five times the worst error of a NumPy model of
+# exactly the kernel's FP32 arithmetic (tests/test_f32_model.py), since FP32 itself errs by
+# ~2e-5 at those logits.
+F32_TOL = {1.0: (F32_MAX_ABS, 1e-5), 8.0: (1e-4, 1e-5)}
 BF16_MAX_ABS = 1e-2
 BF16_REL_L2 = 5e-3
 # FP32 I/O with split-bf16 matrix-core products ("f32_split"): about five times the

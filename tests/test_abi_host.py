@@ -205,6 +205,21 @@ def test_run_strided_rejects_oversized_span():
     sw.swin3d_wattn_destroy(h)
 
 
+def test_f32_plans():
+    """F32 I/O: 144-slot windows run on the FP32 matrix-core kernel (4), other windows on the
+    vector-ALU kernel (0)."""
+    for kw, kern in [(dict(dtype="f32", head_dim=64), 4), (dict(dtype="f32", head_dim=32), 4),
+                     (dict(dtype="f32", head_dim=64, window=(2, 4, 4), shift=(1, 2, 2)), 0),
+                     (dict(dtype="f32", head_dim=32, window=(4, 8, 8), shift=(2, 4, 4)), 0)]:
+        rc, h = _create(**kw)
+        assert rc == 0, kw
+        info = sw.swin3d_wattn_get_info(h)[1]
+        assert info.kernel == kern, (kw, info.kernel)
+        if kern == 4:
+            assert (info.threads_per_workgroup, info.workgroups) == (256, 1800 * 8)
+        sw.swin3d_wattn_destroy(h)
+
+
 def test_grid_extent_limit():
     """Each grid extent must stay below 2^24 (the kernels' index arithmetic)."""
     rc, h = _create(B=1, D=2, H=6, W=(1 << 24) - 12)

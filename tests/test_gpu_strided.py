@@ -22,19 +22,22 @@ CASES = [
     ("tiny_f32", None, None, None, None, None, None, None, None, -math.inf),
     ("ragged_bf16", 2, 3, 7, 13, 3, 64, (1, 5, 11), "bf16", -math.inf),
     ("ragged_f32", 1, 4, 44, 30, 2, 32, (1, 3, 6), "f32", -100.0),
+    ("ragged_f32_dh64", 2, 3, 7, 13, 3, 64, (1, 5, 11), "f32", -math.inf),
+    ("f32_window_2x4x4", 1, 4, 10, 13, 2, 32, (1, 2, 3), "f32", -100.0, (2, 4, 4)),  # vector-ALU kernel
 ]
 
 
 def _workload(case):
-    name, B, D, H, W, h, dh, shift, dt, _ = case
+    name, B, D, H, W, h, dh, shift, dt = case[:9]
+    window = case[10] if len(case) > 10 else (2, 6, 12)
     if B is None:
         return datagen.WORKLOADS[name]
-    return datagen.small_workload(name, B, D, H, W, h, dh, (2, 6, 12), shift, dt, seed=23)
+    return datagen.small_workload(name, B, D, H, W, h, dh, window, shift, dt, seed=23)
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_fused_qkv_and_wide_output(case):
-    wl, bias = _workload(case), case[-1]
+    wl, bias = _workload(case), case[9]
     x = device_inputs(wl)
     contiguous = run_gpu(wl, bias, x)
     B, D, H, W, h, dh = wl.shape
