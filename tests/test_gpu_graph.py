@@ -13,9 +13,13 @@ from _gpu import device_inputs, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,plan_dtype", [("stage3_pad", "bf16"), ("stage3_pad_f32_split", "f32_split")])
+STREAM_WL = datagen.small_workload("graph_w2x12x12", 1, 4, 36, 48, 4, 64, (2, 12, 12), (1, 6, 6), "bf16", seed=61)
+
+
+@pytest.mark.parametrize("name,plan_dtype", [("stage3_pad", "bf16"), ("stage3_pad_f32_split", "f32_split"),
+                                             ("stage3_pad_f32", "f32"), ("graph_w2x12x12", "bf16")])
 def test_graph_replays_match_eager(name, plan_dtype):
-    wl = datagen.WORKLOADS[name]
+    wl = STREAM_WL if name == STREAM_WL.name else datagen.WORKLOADS[name]
     x = device_inputs(wl)
     plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=plan_dtype, scale=wl.scale,
                    cross_region_bias=-math.inf)
@@ -41,3 +45,30 @@ def test_graph_replays_match_eager(name, plan_dtype):
         torch.cuda.synchronize()
         assert torch.equal(out.view(ibits), eager.view(ibits)), f"replay {rep}"
     say(f"[gpu] graph {name}: 4 replays bit-identical to eager")
+
+
+def test_graph_replays_adaln():
+    wl = datagen.AdalnWorkload("graph_adaln", 2, 700, 512, "bf16", "f32", "f32", seed=62)
+    a = datagen.adaln_inputs(wl)
+    x = datagen.to_torch(a["x"], "bf16").cuda()
+    res = datagen.to_torch(a["res"], "f32").cuda()
+    g, b = (torch.from_numpy(a[k]).cuda() for k in ("gamma", "beta"))
+    eager = sw.adaln_residual(x, res, g, b, wl.eps)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sw.adaln_residual(x, res, g, b, wl.eps, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        sw.adaln_residual(x, res, g, b, wl.eps, out=out)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
+    say("[gpu] graph adaln: 4 replays bit-identical to eager")
