@@ -245,7 +245,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the attention shards by head or batch with no communication, but no multi-GPU "
               "path is built", file=sys.stderr)
         sys.exit(2)
