@@ -49,7 +49,8 @@ def test_bf16_stage_full(name, bias):
 
 RAGGED = [
     # (B, D, H, W, heads, dh, shift, dtype)
-    (2, 3, 7, 13, 3, 64, (1, 5, 11), "bf16"),   # padding on every axis, large shifts
+    (2, 3, 7, 13, 3, 64, (1, 5, 11), "bf16"),   # padding on every axis, large shifts (each window's
+                                                #   real tokens lie in one region: a padding case)
     (1, 4, 44, 30, 2, 64, (1, 3, 6), "bf16"),   # pad != shift along H
     (1, 2, 6, 12, 1, 64, (0, 0, 0), "bf16"),    # a single unmasked window
     (1, 1, 1, 1, 2, 64, (1, 3, 6), "bf16"),     # a single real token

@@ -48,7 +48,7 @@ def test_zero_shift_matches_sdpa_per_window():
 
 
 # ---------------------------------------------------------------- P3: grid brute force
-@pytest.mark.parametrize("bias", [-100.0, NEG_INF])
+@pytest.mark.parametrize("bias", [-100.0, NEG_INF, -2.5])
 @pytest.mark.parametrize("shape,shift", [
     ((1, 2, 12, 24, 2, 4), (1, 3, 6)),     # tiny workload grid, every window masked
     ((1, 4, 45, 90, 1, 3), (1, 3, 6)),     # stage-3 grid with padding (pad == shift per axis)
@@ -64,7 +64,7 @@ def test_matches_grid_brute_force(shape, shift, bias):
 
 
 # ---------------------------------------------------------------- P4: SDPA with the mask
-@pytest.mark.parametrize("bias", [-100.0, NEG_INF])
+@pytest.mark.parametrize("bias", [-100.0, NEG_INF, -2.5])
 def test_matches_sdpa_with_float_mask(bias):
     """Per window: SDPA (float64, CPU) with a float mask of `bias` where labels
     differ and -inf on padding keys equals the oracle on real query rows."""
@@ -122,13 +122,15 @@ def test_q_zero_exclusion_gives_region_mean():
                                        rtol=0, atol=1e-14)
 
 
-def test_q_zero_bias_closed_form():
-    """Under -100, Q = 0: O_i = (sum_same V + e^-100 sum_other V) / (n_same + e^-100 n_other)."""
+@pytest.mark.parametrize("bias", [-100.0, -1.5])
+def test_q_zero_bias_closed_form(bias):
+    """Q = 0 under a finite bias b: O_i = (sum_same V + e^b sum_other V) / (n_same + e^b n_other)
+    (at -100 the other regions all but vanish; at -1.5 they weigh in)."""
     shape, shift = (1, 2, 12, 24, 1, 2), (1, 3, 6)
     v = _rand(shape, 71)
-    o = oracle.swin3d_window_attention(np.zeros(shape), _rand(shape, 72), v, WIN, shift, 0.3, -100.0)
+    o = oracle.swin3d_window_attention(np.zeros(shape), _rand(shape, 72), v, WIN, shift, 0.3, bias)
     from _pins import token_groups
-    e = math.exp(-100.0)
+    e = math.exp(bias)
     for (b, _), toks in token_groups((2, 12, 24), WIN, shift, 1).items():
         coords = np.array([g for g, _ in toks])
         bits = [bb for _, bb in toks]
