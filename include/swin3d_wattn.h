@@ -86,7 +86,7 @@ typedef struct {
 typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 
 /* Validate *desc and build a plan. Host-only: no device is touched.
- * Supported: dtype BF16 with head_dim 64 or 128, any window with
+ * Supported: dtype BF16 with head_dim 32, 64 or 128, any window with
  * wd*wh*ww <= 4096 and heads < 65536 (N = 144 at head_dim 64 runs the
  * single-tile kernel; every other case streams K and V through LDS in
  * 48- or 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with

@@ -93,7 +93,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     if (d.head_dim == 64 && N == 144 && d.heads < 65536) {
       kernel = d.dtype == SWIN3D_WATTN_BF16 ? 1 : 2;
       threads = 256;
-    } else if (d.dtype == SWIN3D_WATTN_BF16 && (d.head_dim == 64 || d.head_dim == 128) && d.heads < 65536) {
+    } else if (d.dtype == SWIN3D_WATTN_BF16 && (d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128) &&
+               d.heads < 65536) {
       kernel = 3;  // K and V streamed through LDS
       // block shape: 3 waves / 48-key chunks where that wastes no slot and 64 would, else 4 / 64
       threads = (N % 64 != 0 && N % 48 == 0) ? 192 : 256;
@@ -114,8 +115,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   int64_t workgroups = n_windows * d.heads;
   if (kernel == 3) {
     // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of
-    // 16 slots per wave and query tile, two tiles per wave at head_dim 64
-    const int64_t qblock = (int64_t)(threads / 64) * 16 * (d.head_dim == 64 ? 2 : 1);
+    // 16 slots per wave and query tile, two tiles per wave at head_dim 32 and 64
+    const int64_t qblock = (int64_t)(threads / 64) * 16 * (d.head_dim <= 64 ? 2 : 1);
     const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, qblock);
     if (gx >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
     workgroups = gx * d.heads;

@@ -1,5 +1,5 @@
-// Swin3D shifted-window attention for any window size and head_dim 64 or
-// 128, BF16 I/O, K and V streamed through LDS, for gfx950 (MI355X).
+// Swin3D shifted-window attention for any window size and head_dim 32, 64
+// or 128, BF16 I/O, K and V streamed through LDS, for gfx950 (MI355X).
 //
 // The Flash-Aurora README ("CuTe DSL window attention") keeps K and V of a
 // whole window in one shared-memory tile when it fits and otherwise falls
@@ -8,8 +8,8 @@
 // single-tile kernel; this one serves every other window and head_dim 128.
 //
 // Work: one workgroup per (window, head, block of query slots), QT tiles of
-// 16 queries per wave (two at head_dim 64, where each K and V operand read
-// from LDS serves both, one at head_dim 128); K and V of the window pass
+// 16 queries per wave (two at head_dim 32 and 64, where each K and V operand
+// read from LDS serves both, one at head_dim 128); K and V of the window pass
 // through LDS in chunks of key slots,
 // double-buffered: while the waves work on chunk c, each thread holds its
 // part of chunk c + 1 in registers and writes it to the other buffer
@@ -98,9 +98,17 @@ struct StreamParams {
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
-// byte offset of 16-byte chunk c of row r; the XOR touches the low three bits of c only
+// the row swizzle within the DH / 8 chunks of a row (three bits, two for DH = 32)
 template <int DH>
-__device__ __forceinline__ int row_off(int r, int c) { return r * (DH * 2) + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int swzd(int r) { return swz(r) & (DH / 8 - 1); }
+// byte offset of 16-byte chunk c of row r
+template <int DH>
+__device__ __forceinline__ int row_off(int r, int c) { return r * (DH * 2) + ((c ^ swzd<DH>(r)) << 4); }
+// byte offset of the 8-byte piece of V row `key` that holds dims d .. d + 3 (d a multiple of 4)
+template <int DH>
+__device__ __forceinline__ int v_off(int key, int d) {
+  return key * (DH * 2) + (((d >> 3) ^ swzd<DH>(key)) << 4) + ((d & 4) << 1);
+}
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
 __device__ __forceinline__ float wave_max16x4(float x) {
@@ -174,7 +182,7 @@ __device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
 }
 
 template <int DH, int WAVES, int KC, int QT>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH == 64 ? (QT == 1 ? 4 : 3) : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? (QT == 1 ? 4 : 3) : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ o, const StreamParams p) {
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
         const int d = dbase(t, qd);
-        const int lo_off = (32 * j + 4 * g4 + e) * (DH * 2) + ((((d >> 3) ^ swz(32 * j + 4 * g4 + e))) << 4) + ((d & 4) << 1);
-        const int hi_off = (32 * j + 16 + 4 * g4 + e) * (DH * 2) + ((((d >> 3) ^ swz(32 * j + 16 + 4 * g4 + e))) << 4) + ((d & 4) << 1);
+        const int lo_off = v_off<DH>(32 * j + 4 * g4 + e, d);
+        const int hi_off = v_off<DH>(32 * j + 16 + 4 * g4 + e, d);
         const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
         const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
         vf[t] = u32x4{a[0], a[1], b[0], b[1]};
@@ -442,7 +450,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH =
       for (int t = 0; t < kT; ++t) {
         const int d = dbase(t, qd);
         const int key = 32 * kJ + 4 * g4 + e;
-        vt[t] = lds_tr(vb, key * (DH * 2) + (((d >> 3) ^ swz(key)) << 4) + ((d & 4) << 1));
+        vt[t] = lds_tr(vb, v_off<DH>(key, d));
       }
 #pragma unroll
       for (int t = 0; t < kT; ++t)
@@ -544,11 +552,13 @@ int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool k48 = p->threads == 192;  // the plan's block shape: 3 waves and 48-key chunks
   hipError_t e;
-  // head_dim 64: two query tiles per wave (each K and V operand read from LDS
-  // serves both); head_dim 128: one, within the register budget
+  // head_dim 32 and 64: two query tiles per wave (each K and V operand read
+  // from LDS serves both); head_dim 128: one, within the register budget
   if (p->desc.head_dim == 128)
     e = k48 ? launch<128, 3, 48, 1>(p, q, k, v, o, stride, s) : launch<128, 4, 64, 1>(p, q, k, v, o, stride, s);
-  else
+  else if (p->desc.head_dim == 64)
     e = k48 ? launch<64, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<64, 4, 64, 2>(p, q, k, v, o, stride, s);
+  else
+    e = k48 ? launch<32, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<32, 4, 64, 2>(p, q, k, v, o, stride, s);
   return (int)e;
 }

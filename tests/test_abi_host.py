@@ -87,7 +87,7 @@ def test_masked_window_count_matches_oracle_labels():
     (dict(shift=(1, 6, 6)), -1), (dict(dtype=7), -1), (dict(scale=float("nan")), -1),
     (dict(scale=float("inf")), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
     (dict(cross_region_bias=float("nan")), -1), (dict(cross_region_bias=1.0), -1),
-    (dict(head_dim=256), -2), (dict(head_dim=32), -2), (dict(head_dim=96), -2), (dict(window=(2, 6, 6)), -1),
+    (dict(head_dim=256), -2), (dict(head_dim=16), -2), (dict(head_dim=96), -2), (dict(window=(2, 6, 6)), -1),
     (dict(window=(4, 8, 12), shift=(1, 3, 3), dtype="f32", head_dim=64), -2),
     (dict(dtype="f32", head_dim=48), -2),
     (dict(B=2, D=4, H=46341, W=46341), -2),
@@ -101,12 +101,13 @@ def test_create_rejects(kw, code):
 def test_streaming_plans():
     """bf16 windows other than 144 slots, or head_dim 128, go to the K/V-streaming kernel (3):
     3 waves and 48-key chunks where N is a multiple of 48 but not of 64, else 4 waves and 64;
-    16 query slots per wave at head_dim 128, 32 at head_dim 64."""
+    16 query slots per wave at head_dim 128, 32 at head_dim 32 and 64."""
     for kw, wg, thr in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 1 * 8, 256),     # N = 72: 1 x 128
                         (dict(head_dim=128), 1800 * 3 * 8, 192),                          # N = 144: 3 x 48
                         (dict(window=(2, 12, 12), shift=(1, 6, 6)), 904 * 3 * 8, 192),    # N = 288: 3 x 96
                         (dict(window=(4, 12, 24), shift=(2, 6, 12)), 232 * 9 * 8, 256),   # N = 1152 = 9 x 128
-                        (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8, 256)]:
+                        (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8, 256),
+                        (dict(head_dim=32), 1800 * 2 * 8, 192)]:                          # N = 144: 2 x 96
         rc, h = _create(**kw)
         assert rc == 0, kw
         rc2, info = sw.swin3d_wattn_get_info(h)

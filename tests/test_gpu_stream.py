@@ -29,6 +29,8 @@ SMALL = [
     wl_of("single_token", 1, 1, 1, 1, 2, 128, (2, 6, 12), (1, 3, 6)),
     wl_of("w3x12x12", 1, 6, 24, 24, 2, 128, (3, 12, 12), (1, 6, 6)),     # N = 432: 9 chunks of 48
     wl_of("w16x16x16_max", 1, 16, 16, 20, 1, 64, (16, 16, 16), (8, 4, 10)),  # N = 4096, the largest window
+    wl_of("dh32", 1, 4, 13, 25, 3, 32, (2, 6, 12), (1, 3, 6)),           # head_dim 32, N = 144
+    wl_of("dh32_w2x6x6", 2, 3, 10, 14, 2, 32, (2, 6, 6), (1, 3, 3)),      # head_dim 32, N = 72
 ]
 
 

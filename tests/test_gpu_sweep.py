@@ -34,7 +34,7 @@ def _cases(n=48, seed=2024):
         B = int(rng.integers(1, 3))
         heads = int(rng.integers(1, 4))
         if kind.startswith("bf16"):
-            dh = 64 if kind == "bf16_144" else int(rng.choice([64, 128]))
+            dh = 64 if kind == "bf16_144" else int(rng.choice([32, 64, 128]))
             io, plan = "bf16", "bf16"
         elif kind == "f32_split":
             dh, io, plan = 64, "f32", "f32_split"
