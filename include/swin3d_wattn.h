@@ -88,8 +88,10 @@ typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 /* Validate *desc and build a plan. Host-only: no device is touched.
  * Supported: dtype BF16 with head_dim 32, 64 or 128, any window with
  * wd*wh*ww <= 4096 and heads < 65536 (N = 144 at head_dim 64 runs the
- * single-tile kernel; every other case streams K and V through LDS in
- * 48- or 64-key chunks, the pages' multi-stage fallback); dtype F32_SPLIT with
+ * single-tile kernel, N x head_dim = 144 x 128 and 288 x 64 a whole-window
+ * kernel that holds K and V of the window in LDS at two workgroups per CU;
+ * every other case streams K and V through LDS in 48- or 64-key chunks, the
+ * pages' multi-stage fallback); dtype F32_SPLIT with
  * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
  * or 64 and wd*wh*ww <= 256 (wd*wh*ww = 144 with heads < 65536 on the matrix
  * cores, other windows on the vector ALU). B*D*H*W must be < 2^31 and each
@@ -187,7 +189,8 @@ typedef struct {
   int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel,
                                2 = f32 split-bf16 matrix-core kernel, 3 = bf16 matrix-core
                                kernel with K/V streamed through LDS, 4 = f32 matrix-core
-                               kernel */
+                               kernel, 5 = bf16 matrix-core kernel with the whole window's
+                               K/V in LDS (N x head_dim = 144 x 128 or 288 x 64) */
 } swin3d_wattn_info_t;
 
 /* Fill *info for a plan. Host-only. Returns 0 or EINVAL. */

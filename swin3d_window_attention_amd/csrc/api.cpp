@@ -93,6 +93,10 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     if (d.head_dim == 64 && N == 144 && d.heads < 65536) {
       kernel = d.dtype == SWIN3D_WATTN_BF16 ? 1 : 2;
       threads = 256;
+    } else if (d.dtype == SWIN3D_WATTN_BF16 && ((d.head_dim == 128 && N == 144) || (d.head_dim == 64 && N == 288)) &&
+               d.heads < 65536) {
+      kernel = 5;  // the whole window's K and V in LDS, two workgroups per CU
+      threads = 256;
     } else if (d.dtype == SWIN3D_WATTN_BF16 && (d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128) &&
                d.heads < 65536) {
       kernel = 3;  // K and V streamed through LDS
@@ -253,6 +257,7 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
                 : plan->kernel == 2 ? wattn_launch_f32x3(plan, q, k, v, o, st, stream)
                 : plan->kernel == 3 ? wattn_launch_stream(plan, q, k, v, o, st, stream)
                 : plan->kernel == 4 ? wattn_launch_f32m(plan, q, k, v, o, st, stream)
+                : plan->kernel == 5 ? wattn_launch_window(plan, q, k, v, o, st, stream)
                                     : wattn_launch_f32(plan, q, k, v, o, st, stream);
   return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }

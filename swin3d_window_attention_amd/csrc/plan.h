@@ -15,8 +15,9 @@ struct swin3d_wattn_plan {
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
   int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA (N = 144, dh 64), 2: f32 split-bf16 MFMA,
-                            // 3: bf16 MFMA with K/V streamed (any N, dh 64 or 128),
-                            // 4: f32 MFMA (N = 144, dh 32 or 64)
+                            // 3: bf16 MFMA with K/V streamed (any N, dh 32, 64 or 128),
+                            // 4: f32 MFMA (N = 144, dh 32 or 64),
+                            // 5: bf16 MFMA, whole window in LDS (N x dh = 144 x 128 or 288 x 64)
   int64_t workgroups;       // workgroups one run launches
   int32_t threads;          // threads per workgroup
   float c2;                 // scale * log2(e)
@@ -42,6 +43,8 @@ int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, 
 int wattn_launch_f32x3(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                        const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                        const swin3d_wattn_strides_t* stride, void* stream);
+int wattn_launch_window(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                         const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_f32m(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                       const swin3d_wattn_strides_t* stride, void* stream);

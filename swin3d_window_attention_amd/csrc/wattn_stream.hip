@@ -52,6 +52,9 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 // no instruction.
 #define ST_BEFORE(a) asm volatile("" : "+v"(a))
 #define ST_AFTER(c) asm volatile("" : "+v"(c))
+// The same, but LDS instructions stay in place too: used where the source
+// issues LDS reads a fixed distance ahead of the MFMAs that consume them.
+#define ST_PIN_MFMA_LDS() __builtin_amdgcn_sched_barrier(0x676)
 
 constexpr uint32_t kPadSlot = 8;
 
@@ -500,11 +503,253 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   }
 }
 
-template <int DH, int WAVES, int KC, int QT>
-hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
-                  const swin3d_wattn_strides_t* st, hipStream_t s) {
-  constexpr int kQB = 16 * WAVES * QT;
-  constexpr int kKC = KC;
+// ---------------------------------------------------------------------------
+// Whole-window variant for the shapes whose K and V together fill half of
+// the LDS: N x head_dim = 18432 (144 x 128, 288 x 64), 72 KB of K and V plus
+// the tables, two workgroups per CU. This is the single-tile case of the
+// README's CuTe kernel on a 160 KB LDS: the window's K and V are staged once,
+// four waves loop over its query tiles (tile wave + 4 i), and each tile's
+// softmax takes one pass over all N keys, so nothing is rescaled and no
+// query block re-reads K and V. Index map, stand-in tokens, mask k-step,
+// operand layouts and the output stores are the streaming kernel's.
+// ---------------------------------------------------------------------------
+template <int DH, int NT>
+struct WinLds {
+  static constexpr int kTensor = 16 * NT * DH * 2;  // K (or V) of the whole window
+  static constexpr int kXt = 2 * kTensor;           // key then query feature tables, 72 x 16 B
+  static constexpr int kCode = kXt + 72 * 16;       // region code of each slot
+  static constexpr int kBytes = kCode + 16 * NT;
+};
+
+template <int DH, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wattn_window_item(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, const StreamParams p) {
+  using L = WinLds<DH, NT>;
+  constexpr int kThreads = 256;
+  constexpr int kWaves = 4;
+  constexpr int kN = 16 * NT;                          // slots of the window (= N)
+  constexpr int kS = DH / 32;                          // 32-dim k-steps of Q K^T
+  constexpr int kT = DH / 16;                          // 16-dim output tiles
+  constexpr int kCh = DH / 8;                          // 16-byte chunks per row
+  constexpr int kPer = (kN * kCh + kThreads - 1) / kThreads;  // 16-byte loads per thread and tensor
+  constexpr int kMaxQT = (NT + kWaves - 1) / kWaves;   // query tiles per wave (at most)
+  constexpr int kJ = kN / 32;                          // whole 32-key steps of P V
+  constexpr bool kTail = kN % 32 != 0;                 // plus one 16-key step
+  __shared__ __align__(16) uint8_t smem[L::kBytes];
+  uint8_t* codeS = smem + L::kCode;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  // grid (window, head), x fastest: the workgroups in flight read one head of
+  // many neighbouring windows
+  const int head = blockIdx.y;
+  const WinPos cur = decode_window(p, blockIdx.x);
+  const size_t hoff = (size_t)head * DH;
+
+  // ---- gather: K and V rows to registers (then LDS), the Q operands of this
+  // wave's tiles to registers; every load leaves before the first barrier ----
+  u32x4 kr[kPer], vr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int piece = tid + kThreads * j;
+    if (piece < kN * kCh) {
+      int32_t t;
+      uint32_t unused;
+      map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
+      kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
+      vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
+    }
+  }
+  int32_t qtok[kMaxQT];
+  uint32_t qcode[kMaxQT];
+  bf16x8_t qop[kMaxQT][kS];
+#pragma unroll
+  for (int i = 0; i < kMaxQT; ++i) {
+    const int qt = wave + kWaves * i;
+    qcode[i] = kPadSlot;
+    if (qt < NT) {
+      map_slot(p, cur, (uint32_t)(qt * 16 + l16), qtok[i], qcode[i]);
+#pragma unroll
+      for (int s = 0; s < kS; ++s)
+        qop[i][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[i] * p.sq + hoff + 32 * s + 8 * g4));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int piece = tid + kThreads * j;
+    if (piece < kN * kCh) {
+      const int r = piece / kCh, c = piece % kCh;
+      *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, c)) = kr[j];
+      *reinterpret_cast<u32x4*>(smem + L::kTensor + row_off<DH>(r, c)) = vr[j];
+    }
+  }
+  // region codes and mask-feature tables: windows with a cut or padding only
+  if (cur.masked) {
+    for (int r = tid; r < kN; r += kThreads) {
+      int32_t t;
+      uint32_t c;
+      map_slot(p, cur, (uint32_t)r, t, c);
+      codeS[r] = (uint8_t)c;
+    }
+    if (tid < 72) {
+      const int e = tid;
+      const uint32_t ck = (e < 36 ? e : e - 36) >> 2, part = e & 3;
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (e < 36) {
+        const uint32_t beta[3] = {p.beta01 & 0xFFFFu, p.beta01 >> 16, p.beta2 & 0xFFFFu};
+        if (ck == kPadSlot) {
+          if (part == 3) w[0] = p.pad;
+        } else if (part < 3) {
+          const uint32_t bt = beta[part];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (uint32_t)(2 * i) != ck ? bt : 0u;
+            const uint32_t hi = (uint32_t)(2 * i + 1) != ck ? bt : 0u;
+            w[i] = lo | (hi << 16);
+          }
+        }
+      } else if (part < 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = ((uint32_t)(2 * i) == ck ? 0x3F80u : 0u) | ((uint32_t)(2 * i + 1) == ck ? 0x3F800000u : 0u);
+      } else {
+        w[0] = 0x3F80u;
+      }
+      *reinterpret_cast<u32x4*>(smem + L::kXt + e * 16) = w;
+    }
+  }
+  __syncthreads();
+
+  const float c2 = p.c2;
+  const uint8_t* vb = smem + L::kTensor;
+  const int e = l16 >> 2, qd = l16 & 3;
+  const bool odd = g4 & 1;
+#pragma unroll
+  for (int i = 0; i < kMaxQT; ++i) {
+    const int qt = wave + kWaves * i;
+    if (qt >= NT) break;
+
+    // ---- S^T = K Q^T over all key tiles; K operands read kAhead MFMAs ahead.
+    // k-step s of key tile kt is MFMA s NT + kt, so an accumulator's
+    // successive MFMAs lie NT >= 4 apart ----
+    floatx4 S[NT];
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int kSteps = kS * NT;
+      constexpr int kAhead = 8;
+      bf16x8_t kf[kSteps];
+      auto kread = [&](int idx) {
+        const int s = idx / NT, kt = idx % NT;
+        kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+      };
+#pragma unroll
+      for (int idx = 0; idx < kAhead; ++idx) kread(idx);
+#pragma unroll
+      for (int idx = 0; idx < kSteps; ++idx) {
+        const int s = idx / NT, kt = idx % NT;
+        ST_BEFORE(kf[idx]);
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], qop[i][s], S[kt], 0, 0, 0);
+        ST_AFTER(S[kt]);
+        ST_PIN_MFMA_LDS();
+        if (idx + kAhead < kSteps) kread(idx + kAhead);
+      }
+    }
+    if (cur.masked) {
+      const bf16x8_t qxb = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (36 + qcode[i] * 4 + g4) * 16);
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) {
+        bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (codeS[kt * 16 + l16] * 4 + g4) * 16);
+        ST_BEFORE(xf);
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, qxb, S[kt], 0, 0, 0);
+        ST_AFTER(S[kt]);
+        ST_PIN_MFMA();
+      }
+    }
+
+    // ---- softmax in FP32 (log2 domain), P to bf16 in the B-operand layout ----
+    float mx = S[0][0];
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kt][r]);
+    const float nm = -wave_max16x4(mx) * c2;
+    bf16x8_t Pb[kJ > 0 ? kJ : 1];
+    bf16x4_t Pt, prev;
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) {
+      floatx4 P;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        P[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], c2, nm));
+        rs += P[r];
+      }
+      const bf16x4_t pb = __builtin_convertvector(P, bf16x4_t);
+      if (kt & 1)
+        Pb[kt / 2] = __builtin_shufflevector(prev, pb, 0, 1, 2, 3, 4, 5, 6, 7);  // keys 32 (kt / 2) ..
+      else if (kt / 2 < kJ)
+        prev = pb;
+      else
+        Pt = pb;  // the 16-key step (kTail)
+    }
+    const float inv = 1.0f / wave_sum16x4(rs);
+
+    // ---- O^T = V^T P^T: V operands of step j + 1 read during step j ----
+    floatx4 O[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    u32x4 vf[2][kT];
+    auto vread = [&](int j, int buf) {
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        const int d = dbase(t, qd);
+        const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 4 * g4 + e, d)));
+        const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 16 + 4 * g4 + e, d)));
+        vf[buf][t] = u32x4{a[0], a[1], b[0], b[1]};
+      }
+    };
+    vread(0, 0);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      if (j + 1 < kJ) vread(j + 1, (j + 1) & 1);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
+        ST_PIN_MFMA_LDS();
+      }
+    }
+    if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
+      short4_t vt[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) vt[t] = lds_tr(vb, v_off<DH>(32 * kJ + 4 * g4 + e, dbase(t, qd)));
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
+        ST_PIN_MFMA();
+      }
+    }
+
+    // ---- normalise and scatter: one 16-byte store per pair of output tiles ----
+    if (qcode[i] != kPadSlot) {
+      uint16_t* out = o + (size_t)qtok[i] * p.so + hoff;
+#pragma unroll
+      for (int m2 = 0; m2 < kT / 2; ++m2) {
+        const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
+        const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2 + 1] * inv, bf16x4_t));
+        const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
+        *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
+      }
+    }
+  }
+}
+
+// kernel parameters of a plan: nqb query blocks and nchunk key chunks per window
+StreamParams make_params(const swin3d_wattn_plan* pl, const swin3d_wattn_strides_t* st, int nqb, int nchunk) {
   StreamParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
   p.X[0] = d.D;
@@ -518,10 +763,10 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
     for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
   }
   p.N = pl->N;
-  p.nqb = (pl->N + kQB - 1) / kQB;
-  p.nchunk = (pl->N + kKC - 1) / kKC;
+  p.nqb = nqb;
+  p.nchunk = nchunk;
   p.n_windows = (int32_t)pl->n_windows;
-  p.div_qb = make_fastdiv((uint32_t)p.nqb);
+  p.div_qb = make_fastdiv((uint32_t)nqb);
   p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
   p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
   p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
@@ -535,14 +780,35 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
   p.pad = pl->pad_bf16;
+  return p;
+}
+
+template <int DH, int WAVES, int KC, int QT>
+hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+                  const swin3d_wattn_strides_t* st, hipStream_t s) {
+  constexpr int kQB = 16 * WAVES * QT;
+  StreamParams p = make_params(pl, st, (pl->N + kQB - 1) / kQB, (pl->N + KC - 1) / KC);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-  const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)d.heads);
+  const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)pl->desc.heads);
   return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT>), grid,
                          dim3(64 * WAVES), args, 0, s);
+}
+
+template <int DH, int NT>
+hipError_t launch_window(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
+                         const swin3d_wattn_strides_t* st, hipStream_t s) {
+  StreamParams p = make_params(pl, st, 1, 1);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  void* args[] = {&qq, &kk, &vv, &oo, &p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_window_item<DH, NT>),
+                         dim3((unsigned)pl->n_windows, (unsigned)pl->desc.heads), dim3(256), args, 0, s);
 }
 
 }  // namespace
@@ -560,5 +826,14 @@ int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k
     e = k48 ? launch<64, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<64, 4, 64, 2>(p, q, k, v, o, stride, s);
   else
     e = k48 ? launch<32, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<32, 4, 64, 2>(p, q, k, v, o, stride, s);
+  return (int)e;
+}
+
+int wattn_launch_window(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
+                        const swin3d_wattn_strides_t* stride, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the plan admits N x head_dim = 18432 only: 144 x 128 or 288 x 64
+  const hipError_t e = p->desc.head_dim == 128 ? launch_window<128, 9>(p, q, k, v, o, stride, s)
+                                               : launch_window<64, 18>(p, q, k, v, o, stride, s);
   return (int)e;
 }

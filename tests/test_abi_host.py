@@ -98,13 +98,33 @@ def test_create_rejects(kw, code):
     assert rc == code and h is None
 
 
+def test_window_plans():
+    """bf16 windows whose K and V fill half the LDS (N x head_dim = 144 x 128 or 288 x 64) go to
+    the whole-window kernel (5): one workgroup of four waves per (window, head)."""
+    for kw, wg in [(dict(head_dim=128), 1800 * 8),
+                   (dict(head_dim=128, heads=4, shift=(0, 0, 0)), 1800 * 4),
+                   (dict(window=(2, 12, 12), shift=(1, 6, 6)), 900 * 8),
+                   (dict(window=(4, 6, 12), shift=(2, 3, 6), B=2), 2 * 30 * 30 * 8)]:
+        rc, h = _create(**kw)
+        assert rc == 0, kw
+        rc2, info = sw.swin3d_wattn_get_info(h)
+        assert (info.kernel, info.workgroups, info.threads_per_workgroup) == (5, wg, 256), (
+            kw, info.kernel, info.workgroups, info.threads_per_workgroup)
+        sw.swin3d_wattn_destroy(h)
+    for kw in (dict(head_dim=128, dtype=0), dict(head_dim=128, dtype=2), dict(window=(2, 12, 12), dtype=0)):
+        rc, h = _create(**kw)  # FP32 I/O never takes the bf16 kernels
+        assert rc != 0 or sw.swin3d_wattn_get_info(h)[1].kernel != 5, kw
+        if rc == 0:
+            sw.swin3d_wattn_destroy(h)
+
+
 def test_streaming_plans():
-    """bf16 windows other than 144 slots, or head_dim 128, go to the K/V-streaming kernel (3):
-    3 waves and 48-key chunks where N is a multiple of 48 but not of 64, else 4 waves and 64;
-    16 query slots per wave at head_dim 128, 32 at head_dim 32 and 64."""
+    """Other bf16 windows, and head_dim 32, go to the K/V-streaming kernel (3): 3 waves and 48-key
+    chunks where N is a multiple of 48 but not of 64, else 4 waves and 64; 16 query slots per wave
+    at head_dim 128, 32 at head_dim 32 and 64."""
     for kw, wg, thr in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 1 * 8, 256),     # N = 72: 1 x 128
-                        (dict(head_dim=128), 1800 * 3 * 8, 192),                          # N = 144: 3 x 48
-                        (dict(window=(2, 12, 12), shift=(1, 6, 6)), 904 * 3 * 8, 192),    # N = 288: 3 x 96
+                        (dict(window=(3, 12, 12), shift=(1, 6, 6), head_dim=128), 904 * 9 * 8, 192),  # 432: 9 x 48
+                        (dict(window=(3, 12, 12), shift=(1, 6, 6)), 904 * 5 * 8, 192),    # N = 432: 5 x 96
                         (dict(window=(4, 12, 24), shift=(2, 6, 12)), 232 * 9 * 8, 256),   # N = 1152 = 9 x 128
                         (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8, 256),
                         (dict(head_dim=32), 1800 * 2 * 8, 192)]:                          # N = 144: 2 x 96

@@ -22,7 +22,9 @@ CASES = [
     ("bf16_tile", 1, 4, 13, 25, 2, 64, (2, 6, 12), (1, 3, 6), "bf16", "bf16", 1),
     ("f32_split", 1, 4, 13, 25, 2, 64, (2, 6, 12), (1, 3, 6), "f32", "f32_split", 2),
     ("stream_dh64", 1, 4, 12, 22, 2, 64, (2, 6, 6), (1, 3, 3), "bf16", "bf16", 3),
-    ("stream_dh128", 1, 4, 13, 25, 2, 128, (2, 6, 12), (1, 3, 6), "bf16", "bf16", 3),
+    ("stream_dh128", 1, 4, 12, 22, 2, 128, (2, 6, 6), (1, 3, 3), "bf16", "bf16", 3),
+    ("window_dh128", 1, 4, 13, 25, 2, 128, (2, 6, 12), (1, 3, 6), "bf16", "bf16", 5),
+    ("window_w2x12x12", 1, 4, 13, 25, 2, 64, (2, 12, 12), (1, 6, 6), "bf16", "bf16", 5),
     ("f32_mfma", 1, 4, 13, 25, 2, 64, (2, 6, 12), (1, 3, 6), "f32", "f32", 4),
     ("f32_valu", 1, 4, 10, 13, 2, 32, (2, 4, 4), (1, 2, 3), "f32", "f32", 0),
 ]

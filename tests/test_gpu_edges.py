@@ -1,6 +1,6 @@
 """GPU parity at the edges of the launch shape: the largest head count a plan accepts (65,535,
 the y dimension of every attention kernel's launch grid), on a one-window grid, for the bf16
-single-tile, the K/V-streaming and the exact FP32 kernels. Checked against the fp64 oracle on
+single-tile, the K/V-streaming, the whole-window (head_dim 128) and the exact FP32 kernels. Checked against the fp64 oracle on
 the first, a middle and the last head."""
 import math
 
@@ -20,6 +20,7 @@ CASES = [
     # (name, D, H, W, head_dim, window, shift, dtype, kernel)
     ("max_heads_bf16", 2, 6, 12, 64, (2, 6, 12), (1, 3, 6), "bf16", 1),
     ("max_heads_stream", 2, 6, 6, 64, (2, 6, 6), (1, 3, 3), "bf16", 3),
+    ("max_heads_window", 2, 6, 12, 128, (2, 6, 12), (1, 3, 6), "bf16", 5),
     ("max_heads_f32", 2, 6, 12, 32, (2, 6, 12), (1, 3, 6), "f32", 4),
 ]
 

@@ -1,5 +1,5 @@
-"""GPU parity of the K/V-streaming bf16 kernel (windows other than 144 slots, head_dim 128)
-against the fp64 oracle, with the bf16 acceptance bar."""
+"""GPU parity of the K/V-streaming bf16 kernel (kernel 3: bf16 windows whose K and V do not fit
+the single-tile kernels, and head_dim 32) against the fp64 oracle, with the bf16 acceptance bar."""
 import math
 
 import numpy as np
@@ -21,13 +21,14 @@ def wl_of(name, B, D, H, W, heads, dh, window, shift, seed=41):
 
 SMALL = [
     wl_of("w2x6x6", 1, 4, 12, 24, 2, 64, (2, 6, 6), (1, 3, 3)),        # N = 72: a partial second chunk
-    wl_of("dh128", 1, 4, 12, 24, 2, 128, (2, 6, 12), (1, 3, 6)),       # N = 144 at head_dim 128
     wl_of("w4x8x8_ragged", 2, 5, 13, 17, 2, 128, (4, 8, 8), (2, 4, 4)),  # N = 256, padding on every axis
     wl_of("w1x7x7", 1, 3, 20, 30, 3, 64, (1, 7, 7), (0, 3, 3)),        # N = 49 < one chunk
     wl_of("w4x12x24", 1, 4, 24, 48, 1, 64, (4, 12, 24), (2, 6, 12)),   # N = 1152: 18 chunks
     wl_of("w2x6x6_noshift", 1, 2, 12, 18, 2, 64, (2, 6, 6), (0, 0, 0)),  # no mask step but a partial chunk
-    wl_of("single_token", 1, 1, 1, 1, 2, 128, (2, 6, 12), (1, 3, 6)),
+    wl_of("single_token", 1, 1, 1, 1, 2, 128, (2, 6, 6), (1, 3, 3)),
     wl_of("w3x12x12", 1, 6, 24, 24, 2, 128, (3, 12, 12), (1, 6, 6)),     # N = 432: 9 chunks of 48
+    wl_of("w3x12x12_dh64", 1, 3, 13, 25, 2, 64, (3, 12, 12), (1, 6, 6)),  # the same at head_dim 64, padded
+    wl_of("w2x6x4", 1, 4, 13, 15, 2, 64, (2, 6, 4), (1, 3, 2)),          # N = 48: one 48-key chunk
     wl_of("w16x16x16_max", 1, 16, 16, 20, 1, 64, (16, 16, 16), (8, 4, 10)),  # N = 4096, the largest window
     wl_of("dh32", 1, 4, 13, 25, 3, 32, (2, 6, 12), (1, 3, 6)),           # head_dim 32, N = 144
     wl_of("dh32_w2x6x6", 2, 3, 10, 14, 2, 32, (2, 6, 6), (1, 3, 3)),      # head_dim 32, N = 72
@@ -45,22 +46,14 @@ def test_small_whole_grid(wl, bias):
     check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
 
 
-def test_stage2_grid_head_dim_128():
-    """The stage-2 grid with 8 heads of 128 (same channel count as 16 x 64), heads 0 and 7."""
-    wl = wl_of("stage2_dh128", 1, 4, 90, 180, 8, 128, (2, 6, 12), (1, 3, 6), seed=2)
-    x = device_inputs(wl)
-    for bias in BIASES:
-        o = to_f64(run_gpu(wl, bias, x))
-        ref = oracle_full(wl, bias, [0, 7])
-        check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"heads 0,7 bias={bias}")
-
-
-def test_stage1_grid_window_2x12x12_sampled():
-    wl = datagen.WORKLOADS["stage1_w2x12x12"]
+def test_stage1_grid_window_4x12x24_sampled():
+    """The stage-1 grid with window (4, 12, 24) (N = 1152, K and V of 295 KB per window and head:
+    18 chunks) in the launch configuration the benchmark times, on 12 sampled windows."""
+    wl = datagen.WORKLOADS["stage1_w4x12x24"]
     x = device_inputs(wl, keep_host=True)
     o = run_gpu(wl, -100.0, x)
     assert not torch.isnan(o).any().item()
-    check_sampled(wl, -100.0, o, sample_windows(wl, 24, seed=9), x["host"])
+    check_sampled(wl, -100.0, o, sample_windows(wl, 12, seed=9), x["host"])
 
 
 def test_strided_and_guard():
