@@ -57,6 +57,9 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 #define ST_PIN_MFMA_LDS() __builtin_amdgcn_sched_barrier(0x676)
 
 constexpr uint32_t kPadSlot = 8;
+// online softmax: largest exponent (log2) a P value may reach before the
+// reference max of its row moves
+constexpr float kLazy = 8.0f;
 
 template <int DH, int KC>
 struct Lds {
@@ -101,9 +104,22 @@ struct StreamParams {
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
-// the row swizzle within the DH / 8 chunks of a row (three bits, two for DH = 32)
+// The row swizzle within the DH / 8 chunks of a row. LDS serves 256 bytes a
+// cycle, so what matters is the 16-byte unit within a 256-byte line: rows
+// r mod (256 / 2 DH) pick the part of the line, the swizzled chunk the unit
+// within it. The swizzle takes the remaining low row bits (3 at DH = 64, 4 at
+// 128, 2 at 32), so that one chunk of 16 consecutive rows (a K operand read)
+// covers all 16 units, and four consecutive keys at four dim groups (a
+// transposing V read) take each unit at most twice, in its two 8-byte halves.
 template <int DH>
-__device__ __forceinline__ int swzd(int r) { return swz(r) & (DH / 8 - 1); }
+__device__ __forceinline__ int swzd(int r) {
+  if constexpr (DH == 128)
+    return swz(r) | ((r & 1) << 3);
+  else if constexpr (DH == 64)
+    return swz(r);
+  else
+    return (r >> 2) & 3;
+}
 // byte offset of 16-byte chunk c of row r
 template <int DH>
 __device__ __forceinline__ int row_off(int r, int c) { return r * (DH * 2) + ((c ^ swzd<DH>(r)) << 4); }
@@ -318,18 +334,21 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   __syncthreads();
 
   const float c2 = p.c2;
-  float m[QT], l[QT];
+  float m[QT];
   floatx4 O[QT][kT];
+  floatx4 Ls[QT];  // row sums of P on the matrix core (ones x P^T), rescaled with O
   bf16x8_t qxb[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     m[u] = -INFINITY;
-    l[u] = 0.f;
+    Ls[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kT; ++t) O[u][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     qxb[u] = *reinterpret_cast<const bf16x8_t*>(smem + L::kQt + (qcode[u] * 4 + g4) * 16);
   }
   const int e = l16 >> 2, qd = l16 & 3;
+  const u32x4 kOnes8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+  const u32x2 kOnes4 = u32x2{0x3F803F80u, 0x3F803F80u};
 
   for (int c = 0; c < p.nchunk; ++c) {
     const int buf = c & 1;
@@ -402,22 +421,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mc = fmaxf(mc, S[kt][i]);
-      const float m_new = fmaxf(m[u], wave_max16x4(mc));
-      const float alpha = __builtin_amdgcn_exp2f((m[u] - m_new) * c2);  // 0 on the first chunk
+      // the reference max of a row moves only when the chunk's max exceeds it
+      // by more than kLazy in the exponent (always on the first chunk, where
+      // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
+      // does not depend on the reference
+      const float mc_w = wave_max16x4(mc);
+      const bool grow = (mc_w - m[u]) * c2 > kLazy;
+      const float m_new = grow ? mc_w : m[u];
       const float nm = -m_new * c2;
       floatx4 P[kKT];
-      float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
-          rs += P[kt][i];
-        }
-      l[u] = l[u] * alpha + wave_sum16x4(rs);
-      m[u] = m_new;
+        for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
+      if (__any(grow)) {  // wave-uniform
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
+        Ls[u][0] *= alpha;
 #pragma unroll
-      for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+        for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+      }
+      m[u] = m_new;
 #pragma unroll
       for (int j = 0; j < kJ; ++j)
         Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
@@ -446,6 +469,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
           O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
           ST_PIN_MFMA();
         }
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        u32x4 ones = kOnes8;
+        ST_BEFORE(ones);
+        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[u][j], Ls[u], 0, 0, 0);
+        ST_AFTER(Ls[u]);
+        ST_PIN_MFMA();
+      }
     }
     if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
       short4_t vt[kT];
@@ -462,6 +493,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
           O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
           ST_PIN_MFMA();
         }
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        u32x2 ones = kOnes4;
+        ST_BEFORE(ones);
+        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
+        ST_AFTER(Ls[u]);
+        ST_PIN_MFMA();
+      }
     }
 
     // ---- next chunk into the other buffer (everyone finished chunk c - 1,
@@ -490,7 +529,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     if (qcode[u] != kPadSlot) {
-      const float inv = 1.0f / l[u];
+      const float inv = 1.0f / Ls[u][0];
       uint16_t* out = o + (size_t)qtok[u] * p.so + hoff;
 #pragma unroll
       for (int m2 = 0; m2 < kT / 2; ++m2) {
