@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace {
@@ -135,14 +137,10 @@ __device__ __forceinline__ float wave_max16x4(float x) {
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
 }
-__device__ __forceinline__ float wave_sum16x4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
 
 struct WinPos {
   int b, k[3];
+  uint32_t tok0;  // token of slot 0 when the window has no cut and no padding
   bool masked;
 };
 
@@ -161,6 +159,11 @@ __device__ __forceinline__ WinPos decode_window(const StreamParams& p, uint32_t 
 #pragma unroll
     for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
   it.masked = m;
+  // without a cut or padding no slot wraps or falls outside the grid: slot
+  // (od, oh, ow) is token tok0 + (od H + oh) W + ow
+  it.tok0 = (((uint32_t)it.b * (uint32_t)p.X[0] + (uint32_t)(it.k[0] * p.win[0] + p.shift[0])) * (uint32_t)p.X[1] +
+             (uint32_t)(it.k[1] * p.win[1] + p.shift[1])) * (uint32_t)p.X[2] +
+            (uint32_t)(it.k[2] * p.win[2] + p.shift[2]);
   return it;
 }
 
@@ -189,6 +192,16 @@ __device__ __forceinline__ void map_slot(const StreamParams& p, const WinPos& it
   }
   tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
   code = valid ? c : kPadSlot;
+}
+
+// map_slot for a window without a cut or padding (it.masked false): every
+// slot is a real token of region 0
+__device__ __forceinline__ int32_t map_slot_plain(const StreamParams& p, const WinPos& it, uint32_t n) {
+  const uint32_t o0 = fdiv(n, p.div_hw);
+  const uint32_t r = n - o0 * (uint32_t)(p.win[1] * p.win[2]);
+  const uint32_t o1 = fdiv(r, p.div_w);
+  const uint32_t o2 = r - o1 * (uint32_t)p.win[2];
+  return (int32_t)(it.tok0 + (o0 * (uint32_t)p.X[1] + o1) * (uint32_t)p.X[2] + o2);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) {
@@ -592,31 +605,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // ---- gather: K and V rows to registers (then LDS), the Q operands of this
   // wave's tiles to registers; every load leaves before the first barrier ----
   u32x4 kr[kPer], vr[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int piece = tid + kThreads * j;
-    if (piece < kN * kCh) {
-      int32_t t;
-      uint32_t unused;
-      map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
-      kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
-      vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
-    }
-  }
   int32_t qtok[kMaxQT];
   uint32_t qcode[kMaxQT];
   bf16x8_t qop[kMaxQT][kS];
+  // slot -> token: the full map in windows with a cut or padding, the plain
+  // one elsewhere (a wave-uniform branch)
+  auto gather = [&](auto edge) {
+    constexpr bool kEdge = decltype(edge)::value;
 #pragma unroll
-  for (int i = 0; i < kMaxQT; ++i) {
-    const int qt = wave + kWaves * i;
-    qcode[i] = kPadSlot;
-    if (qt < NT) {
-      map_slot(p, cur, (uint32_t)(qt * 16 + l16), qtok[i], qcode[i]);
-#pragma unroll
-      for (int s = 0; s < kS; ++s)
-        qop[i][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[i] * p.sq + hoff + 32 * s + 8 * g4));
+    for (int j = 0; j < kPer; ++j) {
+      const int piece = tid + kThreads * j;
+      if (piece < kN * kCh) {
+        int32_t t;
+        if (kEdge) {
+          uint32_t unused;
+          map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
+        } else {
+          t = map_slot_plain(p, cur, (uint32_t)(piece / kCh));
+        }
+        kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
+        vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
+      }
     }
-  }
+#pragma unroll
+    for (int i = 0; i < kMaxQT; ++i) {
+      const int qt = wave + kWaves * i;
+      qcode[i] = kPadSlot;
+      if (qt < NT) {
+        if (kEdge) {
+          map_slot(p, cur, (uint32_t)(qt * 16 + l16), qtok[i], qcode[i]);
+        } else {
+          qtok[i] = map_slot_plain(p, cur, (uint32_t)(qt * 16 + l16));
+          qcode[i] = 0;
+        }
+#pragma unroll
+        for (int s = 0; s < kS; ++s)
+          qop[i][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[i] * p.sq + hoff + 32 * s + 8 * g4));
+      }
+    }
+  };
+  if (cur.masked)
+    gather(std::true_type{});
+  else
+    gather(std::false_type{});
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int piece = tid + kThreads * j;
@@ -719,15 +750,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const float nm = -wave_max16x4(mx) * c2;
     bf16x8_t Pb[kJ > 0 ? kJ : 1];
     bf16x4_t Pt, prev;
-    float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
       floatx4 P;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        P[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], c2, nm));
-        rs += P[r];
-      }
+      for (int r = 0; r < 4; ++r) P[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], c2, nm));
       const bf16x4_t pb = __builtin_convertvector(P, bf16x4_t);
       if (kt & 1)
         Pb[kt / 2] = __builtin_shufflevector(prev, pb, 0, 1, 2, 3, 4, 5, 6, 7);  // keys 32 (kt / 2) ..
@@ -736,10 +763,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       else
         Pt = pb;  // the 16-key step (kTail)
     }
-    const float inv = 1.0f / wave_sum16x4(rs);
 
-    // ---- O^T = V^T P^T: V operands of step j + 1 read during step j ----
-    floatx4 O[kT];
+    // ---- O^T = V^T P^T: V operands of step j + 1 read during step j; the
+    // row sums of the same bf16 P from the matrix core (ones x P^T) ----
+    floatx4 O[kT], Ls = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
     u32x4 vf[2][kT];
@@ -761,6 +788,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
         ST_PIN_MFMA_LDS();
       }
+      u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      ST_BEFORE(ones);
+      Ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[j], Ls, 0, 0, 0);
+      ST_AFTER(Ls);
+      ST_PIN_MFMA_LDS();
     }
     if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
       short4_t vt[kT];
@@ -771,7 +803,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
         ST_PIN_MFMA();
       }
+      u32x2 ones = u32x2{0x3F803F80u, 0x3F803F80u};
+      ST_BEFORE(ones);
+      Ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones), __builtin_bit_cast(short4_t, Pt), Ls, 0, 0, 0);
+      ST_AFTER(Ls);
+      ST_PIN_MFMA();
     }
+    const float inv = 1.0f / Ls[0];
 
     // ---- normalise and scatter: one 16-byte store per pair of output tiles ----
     if (qcode[i] != kPadSlot) {

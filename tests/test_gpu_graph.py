@@ -13,13 +13,17 @@ from _gpu import device_inputs, say
 pytestmark = pytest.mark.gpu
 
 
-STREAM_WL = datagen.small_workload("graph_w2x12x12", 1, 4, 36, 48, 4, 64, (2, 12, 12), (1, 6, 6), "bf16", seed=61)
+EXTRA = {w.name: w for w in (
+    datagen.small_workload("graph_w2x12x12", 1, 4, 36, 48, 4, 64, (2, 12, 12), (1, 6, 6), "bf16", seed=61),  # whole window
+    datagen.small_workload("graph_w2x6x6", 1, 4, 36, 48, 4, 64, (2, 6, 6), (1, 3, 3), "bf16", seed=63),      # streaming
+)}
 
 
 @pytest.mark.parametrize("name,plan_dtype", [("stage3_pad", "bf16"), ("stage3_pad_f32_split", "f32_split"),
-                                             ("stage3_pad_f32", "f32"), ("graph_w2x12x12", "bf16")])
+                                             ("stage3_pad_f32", "f32"), ("graph_w2x12x12", "bf16"),
+                                             ("graph_w2x6x6", "bf16")])
 def test_graph_replays_match_eager(name, plan_dtype):
-    wl = STREAM_WL if name == STREAM_WL.name else datagen.WORKLOADS[name]
+    wl = EXTRA[name] if name in EXTRA else datagen.WORKLOADS[name]
     x = device_inputs(wl)
     plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=plan_dtype, scale=wl.scale,
                    cross_region_bias=-math.inf)

@@ -16,12 +16,19 @@ from _gpu import check, say, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=48, seed=2024):
+# windows whose K and V fill half the LDS (N x head_dim = 18432): the whole-window kernel
+WHOLE_WINDOW = [((2, 6, 12), 128), ((1, 12, 12), 128), ((4, 6, 6), 128), ((2, 12, 12), 64), ((4, 6, 12), 64),
+                ((2, 8, 18), 64), ((3, 8, 12), 64)]
+
+
+def _cases(n=54, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        kind = ["bf16", "bf16_144", "f32", "f32_144", "f32_split"][len(out) % 5]
-        if kind in ("bf16_144", "f32_144", "f32_split"):
+        kind = ["bf16", "bf16_144", "f32", "f32_144", "f32_split", "bf16_win"][len(out) % 6]
+        if kind == "bf16_win":
+            window, dh_win = WHOLE_WINDOW[int(rng.integers(len(WHOLE_WINDOW)))]
+        elif kind in ("bf16_144", "f32_144", "f32_split"):
             window = [(2, 6, 12), (1, 12, 12), (4, 6, 6), (2, 8, 9), (3, 6, 8)][int(rng.integers(5))]
         else:
             while True:
@@ -34,7 +41,7 @@ def _cases(n=48, seed=2024):
         B = int(rng.integers(1, 3))
         heads = int(rng.integers(1, 4))
         if kind.startswith("bf16"):
-            dh = 64 if kind == "bf16_144" else int(rng.choice([32, 64, 128]))
+            dh = 64 if kind == "bf16_144" else dh_win if kind == "bf16_win" else int(rng.choice([32, 64, 128]))
             io, plan = "bf16", "bf16"
         elif kind == "f32_split":
             dh, io, plan = 64, "f32", "f32_split"
