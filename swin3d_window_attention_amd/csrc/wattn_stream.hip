@@ -63,15 +63,19 @@ constexpr uint32_t kPadSlot = 8;
 // reference max of its row moves
 constexpr float kLazy = 8.0f;
 
+// key slot -> (token, region code) of kRing chunks, refilled four chunks at a time
+constexpr int kRing = 8;
+
 template <int DH, int KC>
 struct Lds {
   static constexpr int kRow = DH * 2;                // bytes per bf16 row
   static constexpr int kTile = KC * kRow;            // one chunk of K (or V)
-  static constexpr int kBuf = 2 * kTile + 64;        // K, V and the chunk's region codes
+  static constexpr int kBuf = 2 * kTile;             // K and V of one chunk
   static constexpr int kXt = 2 * kBuf;               // key feature table
   static constexpr int kQt = kXt + 9 * 4 * 16;       // query feature table
-  static constexpr int kTok = kQt + 9 * 4 * 16;      // key tokens of two chunks (a ring)
-  static constexpr int kBytes = kTok + 2 * KC * 4;
+  static constexpr int kTok = kQt + 9 * 4 * 16;      // token of each key slot of the ring's chunks
+  static constexpr int kCode = kTok + kRing * KC * 4;  // region code of the same slots
+  static constexpr int kBytes = kCode + kRing * KC;
 };
 
 struct FastDiv {
@@ -267,10 +271,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
   // (piece -> key row piece / kCh, chunk piece % kCh). Chunk 0 maps its own
-  // slots; every later chunk's key tokens were mapped once per slot, two
-  // chunks ahead, into a two-entry ring in LDS (entry c & 1 for chunk c) ----
+  // slots; every later chunk reads its key tokens from a ring in LDS (entry
+  // c % kRing for chunk c) that all threads fill four chunks at a time, one
+  // slot each, four chunks ahead: the slot map costs every wave one
+  // evaluation per four chunks ----
+  static_assert(kThreads == 4 * kKC, "one ring slot per thread and refill");
   u32x4 kr[kLoads], vr[kLoads];
   int32_t* tok_ring = reinterpret_cast<int32_t*>(smem + L::kTok);
+  uint8_t* code_ring = smem + L::kCode;
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -280,19 +288,22 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         uint32_t unused;
         map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
       } else {
-        t = tok_ring[(c & 1) * kKC + piece / kCh];
+        t = tok_ring[(c % kRing) * kKC + piece / kCh];
       }
       kr[i] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
       vr[i] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
     }
   };
-  // token of key slot r of chunk c into the ring, its region code returned
-  auto map_ahead = [&](int c, int r) {
-    int32_t t;
-    uint32_t code;
-    map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
-    tok_ring[(c & 1) * kKC + r] = t;
-    return code;
+  // tokens and region codes of chunks c0 .. c0 + 3 (those that exist) into the ring
+  auto fill_ring = [&](int c0) {
+    const int c = c0 + tid / kKC, r = tid % kKC;
+    if (c < p.nchunk) {
+      int32_t t;
+      uint32_t code;
+      map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
+      tok_ring[(c % kRing) * kKC + r] = t;
+      code_ring[(c % kRing) * kKC + r] = (uint8_t)code;
+    }
   };
 
   // mask-feature tables: also unmasked windows use them when the last chunk
@@ -323,14 +334,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     }
     *reinterpret_cast<u32x4*>(smem + L::kXt + e * 16) = w;
   }
-  // region code of key slot c * kKC + r
-  auto code_of = [&](int c, int r) {
-    int32_t t;
-    uint32_t code;
-    map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
-    return code;
-  };
-
   // chunk 0 into buffer 0
   fetch(0);
 #pragma unroll
@@ -340,10 +343,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, c)) = kr[i];
     *reinterpret_cast<u32x4*>(smem + L::kTile + row_off<DH>(r, c)) = vr[i];
   }
-  if (tid < kKC) smem[2 * L::kTile + tid] = (uint8_t)code_of(0, tid);
-  // chunk 1 ahead: its tokens into the ring, its codes kept for staging
-  uint32_t next_code = 0;
-  if (tid < kKC && p.nchunk > 1) next_code = map_ahead(1, tid);
+  fill_ring(0);  // chunks 0 .. 3
   __syncthreads();
 
   const float c2 = p.c2;
@@ -367,13 +367,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     const int buf = c & 1;
     const uint8_t* kb = smem + buf * L::kBuf;
     const uint8_t* vb = kb + L::kTile;
-    const uint8_t* cb = kb + 2 * L::kTile;
+    const uint8_t* cb = code_ring + (c % kRing) * kKC;
     const bool more = c + 1 < p.nchunk;
     if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
-    // chunk c + 2 ahead, into ring entry c & 1 (chunk c's tokens, last read
-    // by the loads of the previous iteration, before its barrier)
-    uint32_t code2 = 0;
-    if (tid < kKC && c + 2 < p.nchunk) code2 = map_ahead(c + 2, tid);
+    // chunks c + 4 .. c + 7 into the ring entries of chunks c - 4 .. c - 1,
+    // whose last readers (the loads of chunk c - 1, the mask step of chunk
+    // c - 1) finished before the previous barrier
+    if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
 
     // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
     // for the wave's QT query tiles. Consecutive MFMAs take independent
@@ -527,9 +527,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, cc)) = kr[i];
         *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, cc)) = vr[i];
       }
-      if (tid < kKC) nb[2 * L::kTile + tid] = (uint8_t)next_code;
     }
-    next_code = code2;
     __syncthreads();
   }
 
