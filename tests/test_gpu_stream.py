@@ -46,6 +46,27 @@ def test_small_whole_grid(wl, bias):
     check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
 
 
+LARGE_LOGITS = [
+    # Q and K x 8, V ~ U(-1, 1): logits with a spread of hundreds, so the running max of a row
+    # jumps many times across the chunks (the lazy rescale's move and keep branches both run)
+    datagen.small_workload("w4x12x24_qk8", 1, 4, 24, 48, 1, 64, (4, 12, 24), (2, 6, 12), "bf16", 47,
+                           qk_mult=8.0, v_dist="uniform"),
+    datagen.small_workload("w3x12x12_dh128_qk8", 1, 3, 13, 25, 2, 128, (3, 12, 12), (1, 6, 6), "bf16", 48,
+                           qk_mult=8.0, v_dist="uniform"),
+]
+
+
+@pytest.mark.parametrize("wl", LARGE_LOGITS, ids=lambda w: w.name)
+def test_large_logits(wl):
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype="bf16", scale=wl.scale)
+    assert plan.info().kernel == 3
+    x = device_inputs(wl)
+    for bias in BIASES:
+        o = to_f64(run_gpu(wl, bias, x))
+        ref = oracle_full(wl, bias)
+        check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
+
+
 def test_stage1_grid_window_4x12x24_sampled():
     """The stage-1 grid with window (4, 12, 24) (N = 1152, K and V of 295 KB per window and head:
     18 chunks) in the launch configuration the benchmark times, on 12 sampled windows."""

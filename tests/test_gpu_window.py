@@ -42,6 +42,26 @@ def test_small_whole_grid(wl, bias):
     check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
 
 
+LARGE_LOGITS = [
+    # Q and K x 8, V ~ U(-1, 1): nearly one-hot rows with a logit spread of hundreds
+    datagen.small_workload("dh128_qk8", 1, 4, 13, 25, 2, 128, (2, 6, 12), (1, 3, 6), "bf16", 49,
+                           qk_mult=8.0, v_dist="uniform"),
+    datagen.small_workload("w2x12x12_qk8", 1, 4, 13, 25, 2, 64, (2, 12, 12), (1, 6, 6), "bf16", 50,
+                           qk_mult=8.0, v_dist="uniform"),
+]
+
+
+@pytest.mark.parametrize("wl", LARGE_LOGITS, ids=lambda w: w.name)
+def test_large_logits(wl):
+    plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype="bf16", scale=wl.scale)
+    assert plan.info().kernel == 5
+    x = device_inputs(wl)
+    for bias in BIASES:
+        o = to_f64(run_gpu(wl, bias, x))
+        ref = oracle_full(wl, bias)
+        check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
+
+
 def test_stage2_grid_head_dim_128():
     """The stage-2 grid with 8 heads of 128 (same channel count as 16 x 64), heads 0 and 7."""
     wl = wl_of("stage2_dh128", 1, 4, 90, 180, 8, 128, (2, 6, 12), (1, 3, 6), seed=2)
