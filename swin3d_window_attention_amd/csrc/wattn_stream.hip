@@ -1,12 +1,16 @@
 // Swin3D shifted-window attention for any window size and head_dim 32, 64
-// or 128, BF16 I/O, K and V streamed through LDS, for gfx950 (MI355X).
+// or 128, BF16 I/O, for gfx950 (MI355X): two kernels that share the index
+// map, the mask tables and the MFMA layouts.
 //
 // The Flash-Aurora README ("CuTe DSL window attention") keeps K and V of a
 // whole window in one shared-memory tile when it fits and otherwise falls
 // back to a multi-stage variant that streams K/V through double-buffered
 // shared memory. The N = 144, head_dim 64 production shape has its own
-// single-tile kernel; this one serves every other window and head_dim 128.
+// single-tile kernel (four workgroups per CU). Here, wattn_window_item keeps
+// the whole window for N x head_dim = 18432 (144 x 128, 288 x 64: two
+// workgroups per CU), and wattn_stream_item streams every other window.
 //
+// wattn_stream_item:
 // Work: one workgroup per (window, head, block of query slots), QT tiles of
 // 16 queries per wave (two at head_dim 32 and 64, where each K and V operand
 // read from LDS serves both, one at head_dim 128); K and V of the window pass
@@ -17,9 +21,11 @@
 // 64-key chunks, or, where the window size is a multiple of 48 but not of
 // 64 (144, 288, ...), three waves and 48-key chunks, so that no key slot
 // past the window is processed (nor a query slot, where N is a multiple of
-// the query block). Softmax is online in
-// FP32 (log2 domain): running max m and sum l per query, O rescaled by
-// 2^((m_old - m_new) c2) whenever the max grows.
+// the query block; e.g. N = 432). Softmax is online in FP32 (log2 domain):
+// a running reference max m per query that moves only when a chunk's max
+// exceeds it by more than kLazy in the exponent (O and the row sums then
+// rescaled by 2^((m_old - m_new) c2)), row sums of the bf16 P from the
+// matrix core.
 //
 // The index map, the stand-in token for padding slots, the shifted-window
 // bias and the padding exclusion as an extra matrix-core k-step, and the
