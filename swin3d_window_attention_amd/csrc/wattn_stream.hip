@@ -110,7 +110,7 @@ struct StreamParams {
   FastDiv div_qb;  // by query blocks per window
   FastDiv div_b, div_d, div_h;
   FastDiv div_hw, div_w;
-  int64_t sq, sk, sv, so;
+  uint32_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements, < 2^31)
   float c2;
   uint32_t beta01, beta2, pad;
 };
@@ -142,11 +142,18 @@ __device__ __forceinline__ int v_off(int key, int d) {
 }
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
-__device__ __forceinline__ float wave_max16x4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+// max over the four lanes l16 + 16 g4: lane ^ 16 by a swizzle within each
+// half-wave (bit mode: and 0x1F, xor 0x10), lane ^ 32 by a permute whose
+// byte address x32 = 4 (lane ^ 32) the caller computes once
+__device__ __forceinline__ float wave_max16x4(float x, int x32) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
   return x;
 }
+
+// element offset of token t's row in a tensor of token stride s (< 2^31):
+// one 32 x 32 -> 64-bit multiply
+__device__ __forceinline__ size_t row_at(int32_t t, uint32_t s) { return (uint64_t)(uint32_t)t * s; }
 
 struct WinPos {
   int b, k[3];
@@ -272,11 +279,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     map_slot(p, cur, (uint32_t)qslot, qtok[u], qcode[u]);
 #pragma unroll
     for (int s = 0; s < kS; ++s)
-      qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[u] * p.sq + hoff + 32 * s + 8 * g4));
+      qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
   }
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
-  // (piece -> key row piece / kCh, chunk piece % kCh). Chunk 0 maps its own
+  // (key row tid / kCh + i kThreads / kCh, chunk tid % kCh). Chunk 0 maps its own
   // slots; every later chunk reads its key tokens from a ring in LDS (entry
   // c % kRing for chunk c) that all threads fill four chunks at a time, one
   // slot each, four chunks ahead: the slot map costs every wave one
@@ -285,19 +292,23 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   u32x4 kr[kLoads], vr[kLoads];
   int32_t* tok_ring = reinterpret_cast<int32_t*>(smem + L::kTok);
   uint8_t* code_ring = smem + L::kCode;
+  static_assert(kThreads % kCh == 0, "one chunk column per thread");
+  const int my_row = tid / kCh, my_ch = tid % kCh;
+  const uint16_t* kcol = k + hoff + 8 * my_ch;
+  const uint16_t* vcol = v + hoff + 8 * my_ch;
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int piece = tid + kThreads * i;
+      const int r = my_row + (kThreads / kCh) * i;
       int32_t t;
       if (c == 0) {
         uint32_t unused;
-        map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
+        map_slot(p, cur, (uint32_t)r, t, unused);
       } else {
-        t = tok_ring[(c % kRing) * kKC + piece / kCh];
+        t = tok_ring[(c % kRing) * kKC + r];
       }
-      kr[i] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
-      vr[i] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
+      kr[i] = ldg16(kcol + row_at(t, p.sk));
+      vr[i] = ldg16(vcol + row_at(t, p.sv));
     }
   };
   // tokens and region codes of chunks c0 .. c0 + 3 (those that exist) into the ring
@@ -344,10 +355,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   fetch(0);
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int piece = tid + kThreads * i;
-    const int r = piece / kCh, c = piece % kCh;
-    *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, c)) = kr[i];
-    *reinterpret_cast<u32x4*>(smem + L::kTile + row_off<DH>(r, c)) = vr[i];
+    const int r = my_row + (kThreads / kCh) * i;
+    *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, my_ch)) = kr[i];
+    *reinterpret_cast<u32x4*>(smem + L::kTile + row_off<DH>(r, my_ch)) = vr[i];
   }
   fill_ring(0);  // chunks 0 .. 3
   __syncthreads();
@@ -366,6 +376,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     qxb[u] = *reinterpret_cast<const bf16x8_t*>(smem + L::kQt + (qcode[u] * 4 + g4) * 16);
   }
   const int e = l16 >> 2, qd = l16 & 3;
+  const int x32 = (lane ^ 32) << 2;
   const u32x4 kOnes8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
   const u32x2 kOnes4 = u32x2{0x3F803F80u, 0x3F803F80u};
 
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       // by more than kLazy in the exponent (always on the first chunk, where
       // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
       // does not depend on the reference
-      const float mc_w = wave_max16x4(mc);
+      const float mc_w = wave_max16x4(mc, x32);
       const bool grow = (mc_w - m[u]) * c2 > kLazy;
       const float m_new = grow ? mc_w : m[u];
       const float nm = -m_new * c2;
@@ -528,10 +539,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int piece = tid + kThreads * i;
-        const int r = piece / kCh, cc = piece % kCh;
-        *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, cc)) = kr[i];
-        *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, cc)) = vr[i];
+        const int r = my_row + (kThreads / kCh) * i;
+        *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, my_ch)) = kr[i];
+        *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, my_ch)) = vr[i];
       }
     }
     __syncthreads();
@@ -547,7 +557,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   for (int u = 0; u < QT; ++u) {
     if (qcode[u] != kPadSlot) {
       const float inv = 1.0f / Ls[u][0];
-      uint16_t* out = o + (size_t)qtok[u] * p.so + hoff;
+      uint16_t* out = o + row_at(qtok[u], p.so) + hoff;
 #pragma unroll
       for (int m2 = 0; m2 < kT / 2; ++m2) {
         const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[u][2 * m2] * inv, bf16x4_t));
@@ -614,21 +624,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   bf16x8_t qop[kMaxQT][kS];
   // slot -> token: the full map in windows with a cut or padding, the plain
   // one elsewhere (a wave-uniform branch)
+  // load j of thread tid: chunk tid % kCh of row tid / kCh + j kThreads / kCh
+  static_assert(kThreads % kCh == 0, "one chunk column per thread");
+  const int my_row = tid / kCh, my_ch = tid % kCh;
+  const uint16_t* kcol = k + hoff + 8 * my_ch;
+  const uint16_t* vcol = v + hoff + 8 * my_ch;
   auto gather = [&](auto edge) {
     constexpr bool kEdge = decltype(edge)::value;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int piece = tid + kThreads * j;
-      if (piece < kN * kCh) {
+      const int r = my_row + (kThreads / kCh) * j;
+      if (r < kN) {
         int32_t t;
         if (kEdge) {
           uint32_t unused;
-          map_slot(p, cur, (uint32_t)(piece / kCh), t, unused);
+          map_slot(p, cur, (uint32_t)r, t, unused);
         } else {
-          t = map_slot_plain(p, cur, (uint32_t)(piece / kCh));
+          t = map_slot_plain(p, cur, (uint32_t)r);
         }
-        kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 8 * (piece % kCh));
-        vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 8 * (piece % kCh));
+        kr[j] = ldg16(kcol + row_at(t, p.sk));
+        vr[j] = ldg16(vcol + row_at(t, p.sv));
       }
     }
 #pragma unroll
@@ -644,7 +659,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         }
 #pragma unroll
         for (int s = 0; s < kS; ++s)
-          qop[i][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + (size_t)qtok[i] * p.sq + hoff + 32 * s + 8 * g4));
+          qop[i][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[i], p.sq) + hoff + 32 * s + 8 * g4));
       }
     }
   };
@@ -654,11 +669,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     gather(std::false_type{});
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int piece = tid + kThreads * j;
-    if (piece < kN * kCh) {
-      const int r = piece / kCh, c = piece % kCh;
-      *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, c)) = kr[j];
-      *reinterpret_cast<u32x4*>(smem + L::kTensor + row_off<DH>(r, c)) = vr[j];
+    const int r = my_row + (kThreads / kCh) * j;
+    if (r < kN) {
+      *reinterpret_cast<u32x4*>(smem + row_off<DH>(r, my_ch)) = kr[j];
+      *reinterpret_cast<u32x4*>(smem + L::kTensor + row_off<DH>(r, my_ch)) = vr[j];
     }
   }
   // region codes and mask-feature tables: windows with a cut or padding only
@@ -699,6 +713,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   __syncthreads();
 
   const float c2 = p.c2;
+  const int x32 = (lane ^ 32) << 2;
   const uint8_t* vb = smem + L::kTensor;
   const int e = l16 >> 2, qd = l16 & 3;
   const bool odd = g4 & 1;
@@ -751,7 +766,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kt][r]);
-    const float nm = -wave_max16x4(mx) * c2;
+    const float nm = -wave_max16x4(mx, x32) * c2;
     bf16x8_t Pb[kJ > 0 ? kJ : 1];
     bf16x4_t Pt, prev;
 #pragma unroll
@@ -817,7 +832,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 
     // ---- normalise and scatter: one 16-byte store per pair of output tiles ----
     if (qcode[i] != kPadSlot) {
-      uint16_t* out = o + (size_t)qtok[i] * p.so + hoff;
+      uint16_t* out = o + row_at(qtok[i], p.so) + hoff;
 #pragma unroll
       for (int m2 = 0; m2 < kT / 2; ++m2) {
         const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
@@ -853,10 +868,10 @@ StreamParams make_params(const swin3d_wattn_plan* pl, const swin3d_wattn_strides
   p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
   p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
   p.div_w = make_fastdiv((uint32_t)d.window[2]);
-  p.sq = st->q;
-  p.sk = st->k;
-  p.sv = st->v;
-  p.so = st->o;
+  p.sq = (uint32_t)st->q;
+  p.sk = (uint32_t)st->k;
+  p.sv = (uint32_t)st->v;
+  p.so = (uint32_t)st->o;
   p.c2 = pl->c2;
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
