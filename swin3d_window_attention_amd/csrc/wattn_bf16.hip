@@ -138,9 +138,12 @@ __device__ __forceinline__ int qkv_off(int r, int c) { return r * 128 + ((c ^ sw
 // read touch both 8-byte halves of the 16-byte chunks it spans
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
-__device__ __forceinline__ float wave_max16x4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+// max over the four lanes l16 + 16 g4: lane ^ 16 by a swizzle within each
+// half-wave (bit mode: and 0x1F, xor 0x10), lane ^ 32 by a permute whose
+// byte address x32 = 4 (lane ^ 32) the caller computes once
+__device__ __forceinline__ float wave_max16x4(float x, int x32) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
   return x;
 }
 
@@ -253,6 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
+  const int x32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   // grid (window, head): x varies fastest, so the workgroups in flight read
   // one head of many neighbouring windows
   const int head = blockIdx.y;
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
-    mx = wave_max16x4(mx);
+    mx = wave_max16x4(mx, x32);
     const float nm = -mx * c2;
     bf16x8_t Pb[4];
     bf16x4_t Pt;

@@ -98,15 +98,18 @@ __device__ __forceinline__ int qkv_off(int r, int c) { return r * 128 + ((c ^ sw
 // first dim of the 4-dim group q held by output tile t (conflict-free transposed V reads)
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
-__device__ __forceinline__ float wave_max16x4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+// max over the four lanes l16 + 16 g4: lane ^ 16 by a swizzle within each
+// half-wave (bit mode: and 0x1F, xor 0x10), lane ^ 32 by a permute whose
+// byte address x32 = 4 (lane ^ 32) the caller computes once
+__device__ __forceinline__ float wave_max16x4(float x, int x32) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
   return x;
 }
 
-__device__ __forceinline__ float wave_sum16x4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+__device__ __forceinline__ float wave_sum16x4(float x, int x32) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x)));
   return x;
 }
 
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
+  const int x32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   const int head = blockIdx.y;
   const WinPos cur = decode_window(p, blockIdx.x);
   const size_t hoff = (size_t)head * 64;
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
-    mx = wave_max16x4(mx);
+    mx = wave_max16x4(mx, x32);
     const float nm = -mx * c2;
     floatx4 P[kNT];
     float rs = 0.f;
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     split4f(P[8], Pth, Ptl);
 
-    const float inv = 1.0f / wave_sum16x4(rs);
+    const float inv = 1.0f / wave_sum16x4(rs, x32);
 
     // ---- O^T = V^T P^T: Vh Ph, Vl Ph, Vh Pl ----
     const int e = l16 >> 2, qd = l16 & 3;
