@@ -118,6 +118,26 @@ def copy_calibration(nbytes: int, steps: int):
                       "gbs_read_plus_write": 2 * n * 2 / dt / 1e9}), flush=True)
 
 
+def device_copy_gbs(torch, nbytes: int) -> float:
+    """Read + write GB/s of a plain device-to-device copy of nbytes (torch's copy kernel), best of 3
+    rounds of 10, with HIP events on the current stream."""
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    best = float("inf")
+    for _ in range(3):
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(10):
+            dst.copy_(src)
+        en.record()
+        torch.cuda.synchronize()
+        best = min(best, st.elapsed_time(en) / 10)
+    del src, dst
+    return 2 * nbytes / (best / 1e3) / 1e9
+
+
 def write_traffic(prof_dir: str, copy_bytes: int = 536870912):
     """Turn four rocprofv3 --pmc runs into the traffic summary that bench.py reports: FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch) of the stage-1 kernel, each scaled by what the same counter
@@ -320,6 +340,25 @@ def main():
         ms = start.elapsed_time(end) / args.steps
     log(f"[bench] {ms * 1000:.1f} us per step{' (cold cache)' if args.cold else ''}")
 
+    # context, after the timed region: single launches each between their own
+    # events (median and min of 20; the pages' method, the mean of 5 after 2
+    # warm-ups), and a plain device copy for the fraction of what this device
+    # moves in practice
+    def single_launches(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for st, en in evs:
+            st.record(stream)
+            plan.run(x["q"], x["k"], x["v"], o)
+            en.record(stream)
+        torch.cuda.synchronize()
+        return [st.elapsed_time(en) * 1000 for st, en in evs]
+
+    singles = sorted(single_launches(20))
+    for _ in range(2):
+        plan.run(x["q"], x["k"], x["v"], o)
+    pages_mean5 = sum(single_launches(5)) / 5
+    copy_gbs = device_copy_gbs(torch, 1 << 29)
+
     nbytes, flops, nwin = algorithmic_work(wl)
     sec = ms / 1e3
     tokens_per_s = wl.tokens / sec
@@ -377,6 +416,10 @@ def main():
             "traffic": measured_traffic() if headline else None,
         }),
         "mfma": {"achieved_tflops": tflops, "peak_tflops": mfma_peak, "frac": frac_mfma},
+        "single_launch_us": {"median": singles[len(singles) // 2], "min": singles[0], "count": len(singles),
+                             "mean_of_5_after_2_warmups": pages_mean5},
+        "device_copy": {"gbs_read_plus_write": copy_gbs, "bytes": 1 << 29,
+                        "algorithmic_frac_of_copy": gbs / copy_gbs},
         "algorithmic_bytes_per_launch": nbytes,
         "algorithmic_flops_per_launch": flops,
         "cpu_baseline": cpu,
