@@ -35,11 +35,11 @@
 #include <cmath>
 
 #include "plan.h"
+#include "window_map.h"
 
 namespace {
 
-typedef float floatx4 __attribute__((__vector_size__(16)));
-typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+using namespace wmap;
 
 // Matrix-core ordering: consecutive MFMAs use independent accumulators (an
 // MFMA whose accumulator input comes from one of the last few MFMAs reads
@@ -55,7 +55,6 @@ constexpr int kN = 144;
 constexpr int kNT = 9;  // key / query tiles of 16
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr uint32_t kPadSlot = 8;  // region code of a padding slot
 constexpr int kVtPitch = 148;     // floats per transposed-V row (144 keys + 4)
 
 template <int DH>
@@ -67,102 +66,12 @@ struct Lds {
   static constexpr int kBytes = kTok + kN * 4;
 };
 
-// floor(n / d) for 0 <= n < 2^31 as (n * mul) >> shr with shr = 31 + ceil(log2 d)
-// and mul = ceil(2^shr / d) (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
-struct FastDiv {
-  uint32_t mul, shr;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint32_t shr = 31 + l;
-  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
-}
-
 struct AttnParams {
-  int32_t X[3], P[3], shift[3], win[3], nwin[3];
-  int32_t special[3][3];
-  FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
-  FastDiv div_hw, div_w;        // by window slots per depth step, per row
+  Geom g;                       // grid, padding, shift, window
   int64_t sq, sk, sv, so;       // token strides of Q, K, V, O (elements)
   float c2;                     // scale * log2(e)
   float bias_s;                 // cross-region bias / scale (may be -inf)
 };
-
-// max over the four lanes l16 + 16 g4: lane ^ 16 by a swizzle within each
-// half-wave (bit mode: and 0x1F, xor 0x10), lane ^ 32 by a permute whose
-// byte address x32 = 4 (lane ^ 32) the caller computes once
-__device__ __forceinline__ float wave_max16x4(float x, int x32) {
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum16x4(float x, int x32) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x)));
-  return x;
-}
-
-struct WinPos {
-  int b, k[3];
-  bool masked;
-};
-
-__device__ __forceinline__ WinPos decode_window(const AttnParams& p, uint32_t w) {
-  WinPos it;
-  const uint32_t per_d = (uint32_t)(p.nwin[1] * p.nwin[2]);
-  it.b = (int)fdiv(w, p.div_b);
-  w -= (uint32_t)it.b * per_d * (uint32_t)p.nwin[0];
-  it.k[0] = (int)fdiv(w, p.div_d);
-  w -= (uint32_t)it.k[0] * per_d;
-  it.k[1] = (int)fdiv(w, p.div_h);
-  it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
-  bool m = false;
-#pragma unroll
-  for (int a = 0; a < 3; ++a)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
-  it.masked = m;
-  return it;
-}
-
-// Slot n = (od, oh, ow) of the window -> token (padding: the nearest real
-// token, a stand-in whose key weight is 0 and whose query is not written)
-// and region code (one bit per shifted axis: position in [P - s, P)), or
-// kPadSlot for padding.
-__device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, uint32_t n, int32_t& tok,
-                                         uint32_t& code) {
-  int o[3];
-  o[0] = (int)fdiv(n, p.div_hw);
-  const uint32_t r = n - (uint32_t)o[0] * (uint32_t)(p.win[1] * p.win[2]);
-  o[1] = (int)fdiv(r, p.div_w);
-  o[2] = (int)(r - (uint32_t)o[1] * (uint32_t)p.win[2]);
-  int g[3];
-  uint32_t c = 0;
-  bool valid = true;
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    const int pa = it.k[a] * p.win[a] + o[a];
-    int ga = pa + p.shift[a];
-    ga = ga >= p.P[a] ? ga - p.P[a] : ga;
-    valid = valid && ga < p.X[a];
-    g[a] = min(ga, p.X[a] - 1);
-    c |= pa >= p.P[a] - p.shift[a] ? (1u << a) : 0u;
-  }
-  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
-  code = valid ? c : kPadSlot;
-}
-
-// Q, K, V are read once: non-temporal loads
-__device__ __forceinline__ u32x4 ldg16(const float* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-}
 
 // byte offset of 16-byte chunk c of K row r (DH / 4 chunks per row, XOR-swizzled by row)
 template <int DH>
@@ -194,7 +103,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int l16 = lane & 15;
   const int x32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   const int head = blockIdx.y;
-  const WinPos cur = decode_window(p, blockIdx.x);
+  const WinPos cur = decode_window(p.g, blockIdx.x);
   const size_t hoff = (size_t)head * DH;
   // query tiles of this wave: (wave - rot) mod 4 + 4 i; the rotation moves
   // the three-tile share from wave to wave across workgroups
@@ -210,7 +119,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (c < kChunks) {
       int32_t t;
       uint32_t unused;
-      map_slot(p, cur, (uint32_t)(c / kCh), t, unused);
+      map_slot<false>(p.g, cur, (uint32_t)(c / kCh), t, unused);
       kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c % kCh));
       vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
     }
@@ -223,7 +132,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (qt < kNT) {
       int32_t t;
       uint32_t unused;
-      map_slot(p, cur, (uint32_t)(qt * 16 + l16), t, unused);
+      map_slot<false>(p.g, cur, (uint32_t)(qt * 16 + l16), t, unused);
       const float* base = q + (size_t)t * p.sq + hoff + g4 * (DH / 4);
 #pragma unroll
       for (int c = 0; c < kQC; ++c) qf[qi][c] = __builtin_bit_cast(floatx4, ldg16(base + 4 * c));
@@ -245,7 +154,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int r = tid; r < kN; r += kThreads) {
     int32_t t;
     uint32_t c;
-    map_slot(p, cur, (uint32_t)r, t, c);
+    map_slot<false>(p.g, cur, (uint32_t)r, t, c);
     tokS[r] = t;
     codeS[r] = (uint8_t)c;
   }
@@ -353,21 +262,7 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
                   const swin3d_wattn_strides_t* st, hipStream_t s) {
   AttnParams p;
   const swin3d_wattn_desc_t& d = pl->desc;
-  p.X[0] = d.D;
-  p.X[1] = d.H;
-  p.X[2] = d.W;
-  for (int a = 0; a < 3; ++a) {
-    p.P[a] = pl->padded[a];
-    p.shift[a] = d.shift[a];
-    p.win[a] = d.window[a];
-    p.nwin[a] = pl->nwin[a];
-    for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
-  }
-  p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
-  p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
-  p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
-  p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
-  p.div_w = make_fastdiv((uint32_t)d.window[2]);
+  p.g = make_geom(pl);
   p.sq = st->q;
   p.sk = st->k;
   p.sv = st->v;

@@ -38,15 +38,11 @@
 #include <type_traits>
 
 #include "plan.h"
+#include "window_map.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
-typedef __bf16 bf16x4_t __attribute__((__vector_size__(8)));
-typedef short short4_t __attribute__((__vector_size__(8)));
-typedef float floatx4 __attribute__((__vector_size__(16)));
-typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
-typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+using namespace wmap;
 
 // Matrix-core ordering: consecutive MFMAs use independent accumulators (an
 // MFMA whose accumulator input comes from one of the last few MFMAs reads
@@ -64,7 +60,6 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 // issues LDS reads a fixed distance ahead of the MFMAs that consume them.
 #define ST_PIN_MFMA_LDS() __builtin_amdgcn_sched_barrier(0x676)
 
-constexpr uint32_t kPadSlot = 8;
 // online softmax: largest exponent (log2) a P value may reach before the
 // reference max of its row moves
 constexpr float kLazy = 8.0f;
@@ -84,32 +79,12 @@ struct Lds {
   static constexpr int kBytes = kCode + kRing * KC;
 };
 
-struct FastDiv {
-  uint32_t mul, shr;
-};
-
-// floor(n / d) for 0 <= n < 2^31 (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint32_t shr = 31 + l;
-  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
-}
-
 struct StreamParams {
-  int32_t X[3], P[3], shift[3], win[3], nwin[3];
-  int32_t special[3][3];
-  int32_t N;       // slots per window
+  Geom g;          // grid, padding, shift, window
   int32_t nqb;     // query blocks per window
   int32_t nchunk;  // key chunks per window
   int32_t n_windows;
   FastDiv div_qb;  // by query blocks per window
-  FastDiv div_b, div_d, div_h;
-  FastDiv div_hw, div_w;
   uint32_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements, < 2^31)
   float c2;
   uint32_t beta01, beta2, pad;
@@ -141,94 +116,6 @@ __device__ __forceinline__ int v_off(int key, int d) {
   return key * (DH * 2) + (((d >> 3) ^ swzd<DH>(key)) << 4) + ((d & 4) << 1);
 }
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
-
-// max over the four lanes l16 + 16 g4: lane ^ 16 by a swizzle within each
-// half-wave (bit mode: and 0x1F, xor 0x10), lane ^ 32 by a permute whose
-// byte address x32 = 4 (lane ^ 32) the caller computes once
-__device__ __forceinline__ float wave_max16x4(float x, int x32) {
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
-  return x;
-}
-
-// element offset of token t's row in a tensor of token stride s (< 2^31):
-// one 32 x 32 -> 64-bit multiply
-__device__ __forceinline__ size_t row_at(int32_t t, uint32_t s) { return (uint64_t)(uint32_t)t * s; }
-
-struct WinPos {
-  int b, k[3];
-  uint32_t tok0;  // token of slot 0 when the window has no cut and no padding
-  bool masked;
-};
-
-__device__ __forceinline__ WinPos decode_window(const StreamParams& p, uint32_t w) {
-  WinPos it;
-  const uint32_t per_d = (uint32_t)(p.nwin[1] * p.nwin[2]);
-  it.b = (int)fdiv(w, p.div_b);
-  w -= (uint32_t)it.b * per_d * (uint32_t)p.nwin[0];
-  it.k[0] = (int)fdiv(w, p.div_d);
-  w -= (uint32_t)it.k[0] * per_d;
-  it.k[1] = (int)fdiv(w, p.div_h);
-  it.k[2] = (int)(w - (uint32_t)it.k[1] * (uint32_t)p.nwin[2]);
-  bool m = false;
-#pragma unroll
-  for (int a = 0; a < 3; ++a)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
-  it.masked = m;
-  // without a cut or padding no slot wraps or falls outside the grid: slot
-  // (od, oh, ow) is token tok0 + (od H + oh) W + ow
-  it.tok0 = (((uint32_t)it.b * (uint32_t)p.X[0] + (uint32_t)(it.k[0] * p.win[0] + p.shift[0])) * (uint32_t)p.X[1] +
-             (uint32_t)(it.k[1] * p.win[1] + p.shift[1])) * (uint32_t)p.X[2] +
-            (uint32_t)(it.k[2] * p.win[2] + p.shift[2]);
-  return it;
-}
-
-// Slot n of the window -> token (padding and slots >= N: a real stand-in
-// token whose key weight is 0 and whose query is not written) and region code.
-__device__ __forceinline__ void map_slot(const StreamParams& p, const WinPos& it, uint32_t n, int32_t& tok,
-                                         uint32_t& code) {
-  const bool beyond = n >= (uint32_t)p.N;
-  n = beyond ? 0u : n;
-  int o[3];
-  o[0] = (int)fdiv(n, p.div_hw);
-  const uint32_t r = n - (uint32_t)o[0] * (uint32_t)(p.win[1] * p.win[2]);
-  o[1] = (int)fdiv(r, p.div_w);
-  o[2] = (int)(r - (uint32_t)o[1] * (uint32_t)p.win[2]);
-  int g[3];
-  uint32_t c = 0;
-  bool valid = !beyond;
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    const int pa = it.k[a] * p.win[a] + o[a];
-    int ga = pa + p.shift[a];
-    ga = ga >= p.P[a] ? ga - p.P[a] : ga;
-    valid = valid && ga < p.X[a];
-    g[a] = min(ga, p.X[a] - 1);
-    c |= (p.shift[a] > 0 && pa >= p.P[a] - p.shift[a]) ? (1u << a) : 0u;
-  }
-  tok = ((it.b * p.X[0] + g[0]) * p.X[1] + g[1]) * p.X[2] + g[2];
-  code = valid ? c : kPadSlot;
-}
-
-// map_slot for a window without a cut or padding (it.masked false): every
-// slot is a real token of region 0
-__device__ __forceinline__ int32_t map_slot_plain(const StreamParams& p, const WinPos& it, uint32_t n) {
-  const uint32_t o0 = fdiv(n, p.div_hw);
-  const uint32_t r = n - o0 * (uint32_t)(p.win[1] * p.win[2]);
-  const uint32_t o1 = fdiv(r, p.div_w);
-  const uint32_t o2 = r - o1 * (uint32_t)p.win[2];
-  return (int32_t)(it.tok0 + (o0 * (uint32_t)p.X[1] + o1) * (uint32_t)p.X[2] + o2);
-}
-
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-}
-
-__device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
-  typedef short4_t __attribute__((address_space(3))) * lds_ptr;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(smem + byte_off));
-}
 
 template <int DH, int WAVES, int KC, int QT>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? (QT == 1 ? 4 : 3) : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
@@ -264,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   const int qb = (int)(xk - w_hi * (uint32_t)p.nqb);
   const uint32_t wq = 8 * w_hi + (blockIdx.x & 7);
   if (wq >= (uint32_t)p.n_windows) return;  // grid padded to a multiple of 8 windows
-  const WinPos cur = decode_window(p, wq);
+  const WinPos cur = decode_window(p.g, wq);
   const size_t hoff = (size_t)head * DH;
 
   // ---- this wave's QT tiles of 16 queries (tile wave QT + u of the block):
@@ -276,7 +163,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const int qslot = qb * kQB + (wave * QT + u) * 16 + l16;
-    map_slot(p, cur, (uint32_t)qslot, qtok[u], qcode[u]);
+    map_slot(p.g, cur, (uint32_t)qslot, qtok[u], qcode[u]);
 #pragma unroll
     for (int s = 0; s < kS; ++s)
       qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
@@ -303,7 +190,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       int32_t t;
       if (c == 0) {
         uint32_t unused;
-        map_slot(p, cur, (uint32_t)r, t, unused);
+        map_slot(p.g, cur, (uint32_t)r, t, unused);
       } else {
         t = tok_ring[(c % kRing) * kKC + r];
       }
@@ -317,7 +204,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     if (c < p.nchunk) {
       int32_t t;
       uint32_t code;
-      map_slot(p, cur, (uint32_t)(c * kKC + r), t, code);
+      map_slot(p.g, cur, (uint32_t)(c * kKC + r), t, code);
       tok_ring[(c % kRing) * kKC + r] = t;
       code_ring[(c % kRing) * kKC + r] = (uint8_t)code;
     }
@@ -422,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         }
     }
     // mask k-step: the window has a cut or padding, or this chunk runs past N
-    if (cur.masked || (c + 1) * kKC > p.N) {
+    if (cur.masked || (c + 1) * kKC > p.g.N) {
       bf16x8_t xf[kKT];
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
@@ -613,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // grid (window, head), x fastest: the workgroups in flight read one head of
   // many neighbouring windows
   const int head = blockIdx.y;
-  const WinPos cur = decode_window(p, blockIdx.x);
+  const WinPos cur = decode_window(p.g, blockIdx.x);
   const size_t hoff = (size_t)head * DH;
 
   // ---- gather: K and V rows to registers (then LDS), the Q operands of this
@@ -638,9 +525,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         int32_t t;
         if (kEdge) {
           uint32_t unused;
-          map_slot(p, cur, (uint32_t)r, t, unused);
+          map_slot(p.g, cur, (uint32_t)r, t, unused);
         } else {
-          t = map_slot_plain(p, cur, (uint32_t)r);
+          t = map_slot_plain(p.g, cur, (uint32_t)r);
         }
         kr[j] = ldg16(kcol + row_at(t, p.sk));
         vr[j] = ldg16(vcol + row_at(t, p.sv));
@@ -652,9 +539,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       qcode[i] = kPadSlot;
       if (qt < NT) {
         if (kEdge) {
-          map_slot(p, cur, (uint32_t)(qt * 16 + l16), qtok[i], qcode[i]);
+          map_slot(p.g, cur, (uint32_t)(qt * 16 + l16), qtok[i], qcode[i]);
         } else {
-          qtok[i] = map_slot_plain(p, cur, (uint32_t)(qt * 16 + l16));
+          qtok[i] = map_slot_plain(p.g, cur, (uint32_t)(qt * 16 + l16));
           qcode[i] = 0;
         }
 #pragma unroll
@@ -680,7 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int r = tid; r < kN; r += kThreads) {
       int32_t t;
       uint32_t c;
-      map_slot(p, cur, (uint32_t)r, t, c);
+      map_slot(p.g, cur, (uint32_t)r, t, c);
       codeS[r] = (uint8_t)c;
     }
     if (tid < 72) {
@@ -847,27 +734,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 // kernel parameters of a plan: nqb query blocks and nchunk key chunks per window
 StreamParams make_params(const swin3d_wattn_plan* pl, const swin3d_wattn_strides_t* st, int nqb, int nchunk) {
   StreamParams p;
-  const swin3d_wattn_desc_t& d = pl->desc;
-  p.X[0] = d.D;
-  p.X[1] = d.H;
-  p.X[2] = d.W;
-  for (int a = 0; a < 3; ++a) {
-    p.P[a] = pl->padded[a];
-    p.shift[a] = d.shift[a];
-    p.win[a] = d.window[a];
-    p.nwin[a] = pl->nwin[a];
-    for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
-  }
-  p.N = pl->N;
+  p.g = make_geom(pl);
   p.nqb = nqb;
   p.nchunk = nchunk;
   p.n_windows = (int32_t)pl->n_windows;
   p.div_qb = make_fastdiv((uint32_t)nqb);
-  p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
-  p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));
-  p.div_h = make_fastdiv((uint32_t)pl->nwin[2]);
-  p.div_hw = make_fastdiv((uint32_t)(d.window[1] * d.window[2]));
-  p.div_w = make_fastdiv((uint32_t)d.window[2]);
   p.sq = (uint32_t)st->q;
   p.sk = (uint32_t)st->k;
   p.sv = (uint32_t)st->v;
