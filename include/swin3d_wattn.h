@@ -30,10 +30,11 @@
  * FP32 accumulation and an FP32 softmax; P is rounded to bf16 (nearest-even)
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
  * computes everything in FP32 (FP32 matrix-core products for 144-slot
- * windows, the vector ALU for other windows). The bf16 kernel fills the padding slots of a
- * window with the nearest real token and gives them a zero weight, so Q, K
- * and V must be finite: an Inf or NaN there may also reach the windows that
- * border the padding.
+ * windows, the vector ALU for other windows); f32 I/O with F32_SPLIT runs the
+ * products as three bf16 matrix-core products each. The matrix-core kernels
+ * fill the padding slots of a window with the nearest real token and give
+ * them a zero weight, so Q, K and V must be finite: an Inf or NaN there may
+ * also reach the windows that border the padding.
  *
  * Ownership: the caller owns every device buffer. The library allocates no
  * device memory; a plan is a small immutable host object.
