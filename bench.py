@@ -66,34 +66,98 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The fp64 oracle, as it stands, run head by head over the same grid (cycling through the
-    heads again if needed) until about budget_s of wall time has been spent."""
+def _cpu_time():
+    r = resource.getrusage(resource.RUSAGE_SELF)
+    return r.ru_utime + r.ru_stime
+
+
+def cpu_baseline(wl, budget_s: float, bias: float = -100.0):
+    """The fp64 oracle, as it stands, timed on a bounded sample of the same workload for about
+    budget_s of wall time: whole heads of the grid, one call per head (cycling through the heads),
+    where the grid is no larger than the stage-1 one; otherwise seeded batches of 16 random
+    windows, every head, read from the same inputs."""
+    import numpy as np
+
     import datagen
     import oracle
 
-    q, k, v = (datagen.full_f64(wl, t) for t in ("q", "k", "v"))
-    done = 0
-    r0 = resource.getrusage(resource.RUSAGE_SELF)
-    t0 = time.perf_counter()
-    while True:
-        h = done % wl.heads
-        sl = (Ellipsis, slice(h, h + 1), slice(None))
-        oracle.swin3d_window_attention(q[sl], k[sl], v[sl], wl.window, wl.shift, wl.scale, -100.0)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s and done >= wl.heads // 2:
-            break
-    wall = time.perf_counter() - t0
-    r1 = resource.getrusage(resource.RUSAGE_SELF)
-    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
-    del q, k, v
+    grid = (wl.D, wl.H, wl.W)
+    nwin = oracle.window_count(wl.B, grid, wl.window)
+    if wl.tokens * wl.heads * wl.head_dim <= 259200 * 8 * 64:
+        q, k, v = (datagen.full_f64(wl, t) for t in ("q", "k", "v"))
+        done = 0
+        c0, t0 = _cpu_time(), time.perf_counter()
+        while True:
+            h = done % wl.heads
+            sl = (Ellipsis, slice(h, h + 1), slice(None))
+            oracle.swin3d_window_attention(q[sl], k[sl], v[sl], wl.window, wl.shift, wl.scale, bias)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+        del q, k, v
+        frac = done / wl.heads
+        sample = (f"fp64 numpy oracle on the whole {wl.name} grid, one head per call, {done} head pass{'es' if done > 1 else ''} "
+                  f"({done * nwin} window-heads = {frac:.2f} x the workload) in {wall:.1f} s")
+    else:
+        host = {t: datagen.full_io(wl, t) for t in ("q", "k", "v")}
+
+        def fetch(t, b, c):
+            a = host[t][b, c[:, 0], c[:, 1], c[:, 2]]
+            return (datagen.bf16_bits_to_f32(a) if wl.dtype == "bf16" else a).astype(np.float64)
+
+        nw = [oracle.padded_extent(x, w) // w for x, w in zip(grid, wl.window)]
+        rng = np.random.default_rng(12345)
+        done = 0
+        c0, t0 = _cpu_time(), time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            wins = [(int(rng.integers(wl.B)),) + tuple(int(rng.integers(n)) for n in nw) for _ in range(16)]
+            oracle.windows_attention(fetch, wl.B, grid, wl.heads, wl.head_dim, wl.window, wl.shift, wl.scale,
+                                     bias, wins)
+            done += 16
+        wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+        del host
+        frac = done / nwin
+        sample = (f"fp64 numpy oracle on {done} seeded random windows of the {wl.name} grid, all {wl.heads} "
+                  f"heads ({frac:.4f} x the workload) in {wall:.1f} s")
     return {
-        "value": wl.tokens * done / wl.heads / wall,
+        "value": wl.tokens * frac / wall,
         "unit": "tokens/s",
         "cores": max(1, int(round(cpu / wall))),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle on the full stage-1 grid, one head per call, {done} head passes "
-                  f"({done * 1800} window-heads = {done / wl.heads:.2f} x the workload) in {wall:.1f} s",
+        "sample": sample,
+        "cpu_seconds": round(cpu, 2),
+        "cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def cpu_baseline_adaln(wl, a, budget_s: float):
+    """The fp64 AdaLN + residual oracle on consecutive blocks of 4,096 rows of the same inputs
+    (cycling) for about budget_s of wall time."""
+    import numpy as np
+
+    import datagen
+    import oracle.adaln as oadaln
+
+    def f64(x, dt):
+        return (datagen.bf16_bits_to_f32(x) if dt == "bf16" else x).astype(np.float64)
+
+    rows, step, done = wl.rows, 4096, 0
+    c0, t0 = _cpu_time(), time.perf_counter()
+    while time.perf_counter() - t0 < budget_s or done == 0:
+        r = (done * step) % rows
+        sl = slice(r, min(rows, r + step))
+        oadaln.adaln_residual(f64(a["x"][:, sl], wl.x_dtype), f64(a["res"][:, sl], wl.res_dtype),
+                              a["gamma"].astype(np.float64), a["beta"].astype(np.float64), wl.eps)
+        done += 1
+    wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+    n_rows = done * step * wl.B
+    return {
+        "value": n_rows / wall,
+        "unit": "tokens/s",
+        "cores": max(1, int(round(cpu / wall))),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle on {done} blocks of {step} rows x {wl.B} batch of the {wl.name} inputs in {wall:.1f} s",
         "cpu_seconds": round(cpu, 2),
         "cores_available": len(os.sched_getaffinity(0)),
     }
@@ -222,6 +286,10 @@ def bench_adaln(args):
     n = wl.B * wl.rows * wl.C
     nbytes = n * (elt[wl.x_dtype] + elt[wl.res_dtype] + elt[wl.out_dtype]) + 2 * wl.B * wl.C * 4
     gbs = nbytes / (ms / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        cpu = cpu_baseline_adaln(wl, a, args.cpu_budget)
     print(json.dumps({
         "metric": "fused AdaLN + residual tokens/s at the 0.25-degree stage-1 token count",
         "value": wl.B * wl.rows / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -231,7 +299,7 @@ def bench_adaln(args):
         "config": {"workload": wl.name, "B": wl.B, "rows": wl.rows, "C": wl.C, "eps": wl.eps},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes_per_launch": nbytes, "cpu_baseline": None,
+        "algorithmic_bytes_per_launch": nbytes, "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -371,9 +439,9 @@ def main():
     mfma_bound = flops / (mfma_peak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
 
     cpu = None
-    if not args.no_cpu_baseline and headline:
+    if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(wl, args.cpu_budget, args.bias)
 
     line = {
         "metric": METRIC,
