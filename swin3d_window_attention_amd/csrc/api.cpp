@@ -104,8 +104,8 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
       threads = (N % 64 != 0 && N % 48 == 0) ? 192 : 256;
     }
   } else {
-    if ((d.head_dim == 32 || d.head_dim == 64) && N == 144 && d.heads < 65536) {
-      kernel = 4;  // FP32 on the matrix cores
+    if ((d.head_dim == 32 || d.head_dim == 64) && N <= 144 && d.heads < 65536) {
+      kernel = 4;  // FP32 on the matrix cores (tiles of 16 slots, the last one padded)
       threads = 256;
     } else if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
       kernel = 0;

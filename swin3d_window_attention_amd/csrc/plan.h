@@ -16,7 +16,7 @@ struct swin3d_wattn_plan {
   int32_t elem_bytes;
   int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA (N = 144, dh 64), 2: f32 split-bf16 MFMA,
                             // 3: bf16 MFMA with K/V streamed (any N, dh 32, 64 or 128),
-                            // 4: f32 MFMA (N = 144, dh 32 or 64),
+                            // 4: f32 MFMA (N <= 144, dh 32 or 64),
                             // 5: bf16 MFMA, whole window in LDS (N x dh = 144 x 128 or 288 x 64)
   int64_t workgroups;       // workgroups one run launches
   int32_t threads;          // threads per workgroup

@@ -51,18 +51,18 @@ using namespace wmap;
 #define FM_BEFORE(a) asm volatile("" : "+v"(a))
 #define FM_AFTER(c) asm volatile("" : "+v"(c))
 
-constexpr int kN = 144;
-constexpr int kNT = 9;  // key / query tiles of 16
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVtPitch = 148;     // floats per transposed-V row (144 keys + 4)
 
-template <int DH>
+// window of N <= 16 NT slots, NT key / query tiles of 16 (slots N .. 16 NT - 1 are padding)
+template <int DH, int NT>
 struct Lds {
-  static constexpr int kK = 0;                       // K, row-major, 144 x DH floats
-  static constexpr int kVt = kN * DH * 4;            // V^T, DH x 148 floats
+  static constexpr int kN = 16 * NT;
+  static constexpr int kVtPitch = kN + 4;            // floats per transposed-V row (16 rows hit distinct banks)
+  static constexpr int kK = 0;                       // K, row-major, kN x DH floats
+  static constexpr int kVt = kN * DH * 4;            // V^T, DH x kVtPitch floats
   static constexpr int kCode = kVt + DH * kVtPitch * 4;
-  static constexpr int kTok = kCode + kN;            // 4-byte aligned: kN is a multiple of 4
+  static constexpr int kTok = kCode + kN;            // 4-byte aligned: kN is a multiple of 16
   static constexpr int kBytes = kTok + kN * 4;
 };
 
@@ -79,11 +79,14 @@ __device__ __forceinline__ int k_off(int r, int c) {
   return r * (DH * 4) + ((c ^ (r & (DH / 4 - 1))) << 4);
 }
 
-template <int DH>
+template <int DH, int NT, bool kTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wattn_f32m_item(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
     const AttnParams p) {
-  using L = Lds<DH>;
+  using L = Lds<DH, NT>;
+  constexpr int kN = L::kN;                   // slots, N of them real (N > 16 (NT - 1))
+  constexpr int kNT = NT;                     // key / query tiles of 16
+  constexpr int kVtPitch = L::kVtPitch;
   constexpr int kCh = DH / 4;                 // 16-byte chunks per row
   constexpr int kQC = DH / 16;                // 16-byte chunks of a lane's dims (= k-step groups of 4)
   constexpr int kT = DH / 16;                 // 16-dim output tiles
@@ -104,6 +107,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int x32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   const int head = blockIdx.y;
   const WinPos cur = decode_window(p.g, blockIdx.x);
+  // kTail: the last tile holds slots past N (padding), so the mask step always runs
+  const bool masked = cur.masked || kTail;
   const size_t hoff = (size_t)head * DH;
   // query tiles of this wave: (wave - rot) mod 4 + 4 i; the rotation moves
   // the three-tile share from wave to wave across workgroups
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (c < kChunks) {
       int32_t t;
       uint32_t unused;
-      map_slot<false>(p.g, cur, (uint32_t)(c / kCh), t, unused);
+      map_slot<kTail>(p.g, cur, (uint32_t)(c / kCh), t, unused);
       kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c % kCh));
       vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
     }
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (qt < kNT) {
       int32_t t;
       uint32_t unused;
-      map_slot<false>(p.g, cur, (uint32_t)(qt * 16 + l16), t, unused);
+      map_slot<kTail>(p.g, cur, (uint32_t)(qt * 16 + l16), t, unused);
       const float* base = q + (size_t)t * p.sq + hoff + g4 * (DH / 4);
 #pragma unroll
       for (int c = 0; c < kQC; ++c) qf[qi][c] = __builtin_bit_cast(floatx4, ldg16(base + 4 * c));
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int r = tid; r < kN; r += kThreads) {
     int32_t t;
     uint32_t c;
-    map_slot<false>(p.g, cur, (uint32_t)r, t, c);
+    map_slot<kTail>(p.g, cur, (uint32_t)r, t, c);
     tokS[r] = t;
     codeS[r] = (uint8_t)c;
   }
@@ -167,9 +172,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (qt >= kNT) break;
 
     // ---- S^T = K Q^T: k-step s = 4 c + e of lane group kk is dim kk DH/4 + s ----
-    floatx4 S[kNT];
+    // with fewer than four key tiles, k-step s accumulates into set s % kAccS,
+    // so that no MFMA takes its accumulator from one of the three before it
+    constexpr int kAccS = kNT >= 4 ? 1 : kNT == 1 ? 4 : 2;
+    floatx4 S2[kAccS][kNT];
 #pragma unroll
-    for (int kt = 0; kt < kNT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < kAccS; ++a)
+#pragma unroll
+      for (int kt = 0; kt < kNT; ++kt) S2[a][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kQC; ++c) {
       floatx4 kf[kNT];
@@ -180,12 +190,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int kt = 0; kt < kNT; ++kt) {
+          floatx4& acc = S2[(4 * c + e) % kAccS][kt];
           float a = kf[kt][e];
           FM_BEFORE(a);
-          S[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[qi][c][e], S[kt], 0, 0, 0);
-          FM_AFTER(S[kt]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[qi][c][e], acc, 0, 0, 0);
+          FM_AFTER(acc);
           FM_PIN_MFMA();
         }
+    }
+    floatx4 S[kNT];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) {
+      S[kt] = S2[0][kt];
+#pragma unroll
+      for (int a = 1; a < kAccS; ++a) S[kt] += S2[a][kt];
     }
 
     // ---- shifted-window bias (bias / scale) and padding exclusion, added in
@@ -193,7 +211,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // row max is subtracted before scaling, so the largest weights see no
     // rounding of a large scaled logit: p = 2^((s - max) scale log2(e)) ----
     const uint32_t qc = codeS[qt * 16 + l16];
-    if (cur.masked) {
+    if (masked) {
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt) {
         const uint32_t kc4 = *reinterpret_cast<const uint32_t*>(codeS + kt * 16 + 4 * g4);
@@ -257,7 +275,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <int DH>
+template <int DH, int NT>
 hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, const void* v, void* o,
                   const swin3d_wattn_strides_t* st, hipStream_t s) {
   AttnParams p;
@@ -275,7 +293,9 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   const float* vv = static_cast<const float*>(v);
   float* oo = static_cast<float*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_f32m_item<DH>),
+  const void* fn = pl->N < 16 * NT ? reinterpret_cast<const void*>(&wattn_f32m_item<DH, NT, true>)
+                                    : reinterpret_cast<const void*>(&wattn_f32m_item<DH, NT, false>);
+  return hipLaunchKernel(fn,
                          dim3((unsigned)pl->n_windows, (unsigned)d.heads), dim3(kThreads), args, 0, s);
 }
 
@@ -284,7 +304,21 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
 int wattn_launch_f32m(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                       const swin3d_wattn_strides_t* stride, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = p->desc.head_dim == 32 ? launch<32>(p, q, k, v, o, stride, s)
-                                              : launch<64>(p, q, k, v, o, stride, s);
+  // the plan admits N <= 144 (NT = ceil(N / 16) tiles of 16 slots) and head_dim 32 or 64
+  const int nt = (p->N + 15) / 16;
+  const bool d32 = p->desc.head_dim == 32;
+  hipError_t e;
+  switch (nt) {
+    case 1: e = d32 ? launch<32, 1>(p, q, k, v, o, stride, s) : launch<64, 1>(p, q, k, v, o, stride, s); break;
+    case 2: e = d32 ? launch<32, 2>(p, q, k, v, o, stride, s) : launch<64, 2>(p, q, k, v, o, stride, s); break;
+    case 3: e = d32 ? launch<32, 3>(p, q, k, v, o, stride, s) : launch<64, 3>(p, q, k, v, o, stride, s); break;
+    case 4: e = d32 ? launch<32, 4>(p, q, k, v, o, stride, s) : launch<64, 4>(p, q, k, v, o, stride, s); break;
+    case 5: e = d32 ? launch<32, 5>(p, q, k, v, o, stride, s) : launch<64, 5>(p, q, k, v, o, stride, s); break;
+    case 6: e = d32 ? launch<32, 6>(p, q, k, v, o, stride, s) : launch<64, 6>(p, q, k, v, o, stride, s); break;
+    case 7: e = d32 ? launch<32, 7>(p, q, k, v, o, stride, s) : launch<64, 7>(p, q, k, v, o, stride, s); break;
+    case 8: e = d32 ? launch<32, 8>(p, q, k, v, o, stride, s) : launch<64, 8>(p, q, k, v, o, stride, s); break;
+    case 9: e = d32 ? launch<32, 9>(p, q, k, v, o, stride, s) : launch<64, 9>(p, q, k, v, o, stride, s); break;
+    default: e = hipErrorInvalidValue;
+  }
   return (int)e;
 }

@@ -227,17 +227,20 @@ def test_run_strided_rejects_oversized_span():
 
 
 def test_f32_plans():
-    """F32 I/O: 144-slot windows run on the FP32 matrix-core kernel (4), other windows on the
-    vector-ALU kernel (0)."""
-    for kw, kern in [(dict(dtype="f32", head_dim=64), 4), (dict(dtype="f32", head_dim=32), 4),
-                     (dict(dtype="f32", head_dim=64, window=(2, 4, 4), shift=(1, 2, 2)), 0),
-                     (dict(dtype="f32", head_dim=32, window=(4, 8, 8), shift=(2, 4, 4)), 0)]:
+    """F32 I/O: windows of up to 144 slots run on the FP32 matrix-core kernel (4), larger ones
+    (up to 256 slots) on the vector-ALU kernel (0)."""
+    for kw, kern, wg in [(dict(dtype="f32", head_dim=64), 4, 1800 * 8), (dict(dtype="f32", head_dim=32), 4, 1800 * 8),
+                         (dict(dtype="f32", head_dim=64, window=(2, 4, 4), shift=(1, 2, 2)), 4, 2 * 45 * 90 * 8),
+                         (dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)), 4, 4 * 180 * 360 * 8),
+                         (dict(dtype="f32", head_dim=64, window=(2, 8, 9), shift=(1, 4, 4)), 4, 2 * 23 * 40 * 8),
+                         (dict(dtype="f32", head_dim=64, window=(2, 8, 10), shift=(1, 4, 5)), 0, None),
+                         (dict(dtype="f32", head_dim=32, window=(4, 8, 8), shift=(2, 4, 4)), 0, None)]:
         rc, h = _create(**kw)
         assert rc == 0, kw
         info = sw.swin3d_wattn_get_info(h)[1]
         assert info.kernel == kern, (kw, info.kernel)
         if kern == 4:
-            assert (info.threads_per_workgroup, info.workgroups) == (256, 1800 * 8)
+            assert (info.threads_per_workgroup, info.workgroups) == (256, wg), kw
         sw.swin3d_wattn_destroy(h)
 
 

@@ -1,5 +1,5 @@
-"""GPU parity of the exact FP32 matrix-core kernel (plan dtype "f32", 144-slot windows, head_dim 32
-or 64) against the fp64 oracle, with the FP32 bar (1e-5 max abs)."""
+"""GPU parity of the exact FP32 matrix-core kernel (plan dtype "f32", windows of up to 144 slots,
+head_dim 32 or 64) against the fp64 oracle, with the FP32 bar (1e-5 max abs)."""
 import math
 
 import numpy as np
@@ -32,7 +32,19 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+OTHER_WINDOWS = [
+    # windows of fewer than 144 slots: the last tile of 16 slots is partly padding (slots past N)
+    datagen.small_workload("f32m_w2x6x6", 1, 4, 13, 20, 2, 64, (2, 6, 6), (1, 3, 3), "f32", 57),         # N = 72
+    datagen.small_workload("f32m_w1x7x7", 2, 3, 15, 16, 2, 32, (1, 7, 7), (0, 3, 3), "f32", 58),         # N = 49
+    datagen.small_workload("f32m_w2x4x4", 1, 4, 10, 13, 3, 64, (2, 4, 4), (1, 2, 3), "f32", 59),         # N = 32
+    datagen.small_workload("f32m_w2x8x8", 1, 4, 17, 19, 2, 64, (2, 8, 8), (1, 4, 4), "f32", 60),         # N = 128
+    datagen.small_workload("f32m_w1x1x3", 1, 2, 3, 7, 2, 32, (1, 1, 3), (0, 0, 1), "f32", 61),           # N = 3
+    datagen.small_workload("f32m_w1x1x1", 1, 2, 3, 4, 2, 64, (1, 1, 1), (0, 0, 0), "f32", 62),           # N = 1
+    datagen.small_workload("f32m_w3x5x9", 1, 5, 11, 20, 2, 32, (3, 5, 9), (2, 2, 4), "f32", 63),         # N = 135
+]
+
+
+@pytest.mark.parametrize("wl", SMALL + OTHER_WINDOWS, ids=lambda w: w.name)
 @pytest.mark.parametrize("bias", BIASES)
 def test_small_whole_grid(wl, bias):
     plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype="f32", scale=wl.scale)
