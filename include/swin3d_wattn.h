@@ -29,12 +29,12 @@
  * Precision: bf16 I/O uses bf16 matrix-core products for Q K^T and P V with
  * FP32 accumulation and an FP32 softmax; P is rounded to bf16 (nearest-even)
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
- * computes everything in FP32 (FP32 matrix-core products for windows of up
- * to 144 slots, the vector ALU for larger ones); f32 I/O with F32_SPLIT runs the
- * products as three bf16 matrix-core products each. The matrix-core kernels
- * fill the padding slots of a window with the nearest real token and give
- * them a zero weight, so Q, K and V must be finite: an Inf or NaN there may
- * also reach the windows that border the padding.
+ * computes everything in FP32 (FP32 matrix-core products, FP32 softmax);
+ * f32 I/O with F32_SPLIT runs the products as three bf16 matrix-core
+ * products each. The kernels fill the padding slots of a window with the
+ * nearest real token and give them a zero weight, so Q, K and V must be
+ * finite: an Inf or NaN there may also reach the windows that border the
+ * padding.
  *
  * Ownership: the caller owns every device buffer. The library allocates no
  * device memory; a plan is a small immutable host object.
@@ -94,8 +94,7 @@ typedef struct swin3d_wattn_plan* swin3d_wattn_t;
  * every other case streams K and V through LDS in 48- or 64-key chunks, the
  * pages' multi-stage fallback); dtype F32_SPLIT with
  * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
- * or 64 and wd*wh*ww <= 256 (wd*wh*ww <= 144 with heads < 65536 on the matrix
- * cores, larger windows on the vector ALU). B*D*H*W must be < 2^31 and each
+ * or 64, wd*wh*ww <= 256 and heads < 65536 (FP32 matrix cores). B*D*H*W must be < 2^31 and each
  * of D, H, W < 2^24.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
@@ -187,7 +186,7 @@ typedef struct {
   int64_t tokens;           /* B*D*H*W real tokens */
   int64_t workgroups;       /* workgroups one run launches */
   int32_t threads_per_workgroup;
-  int32_t kernel;           /* 0 = f32 vector-ALU kernel, 1 = bf16 matrix-core kernel,
+  int32_t kernel;           /* 1 = bf16 matrix-core kernel (N = 144, head_dim 64),
                                2 = f32 split-bf16 matrix-core kernel, 3 = bf16 matrix-core
                                kernel with K/V streamed through LDS, 4 = f32 matrix-core
                                kernel, 5 = bf16 matrix-core kernel with the whole window's

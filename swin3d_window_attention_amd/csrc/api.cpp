@@ -104,12 +104,9 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
       threads = (N % 64 != 0 && N % 48 == 0) ? 192 : 256;
     }
   } else {
-    if ((d.head_dim == 32 || d.head_dim == 64) && N <= 144 && d.heads < 65536) {
+    if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256 && d.heads < 65536) {
       kernel = 4;  // FP32 on the matrix cores (tiles of 16 slots, the last one padded)
       threads = 256;
-    } else if ((d.head_dim == 32 || d.head_dim == 64) && N <= 256) {
-      kernel = 0;
-      threads = (int32_t)(ceil_div(N, 64) * 64);
     }
   }
   if (kernel < 0) return SWIN3D_WATTN_EUNSUPPORTED;
@@ -253,12 +250,15 @@ extern "C" int swin3d_wattn_run_strided(swin3d_wattn_t plan, const void* q, cons
   }
   if (overlaps(o, span[3], q, span[0]) || overlaps(o, span[3], k, span[1]) || overlaps(o, span[3], v, span[2]))
     return SWIN3D_WATTN_EINVAL;
-  const int e = plan->kernel == 1   ? wattn_launch_bf16(plan, q, k, v, o, st, stream)
-                : plan->kernel == 2 ? wattn_launch_f32x3(plan, q, k, v, o, st, stream)
-                : plan->kernel == 3 ? wattn_launch_stream(plan, q, k, v, o, st, stream)
-                : plan->kernel == 4 ? wattn_launch_f32m(plan, q, k, v, o, st, stream)
-                : plan->kernel == 5 ? wattn_launch_window(plan, q, k, v, o, st, stream)
-                                    : wattn_launch_f32(plan, q, k, v, o, st, stream);
+  int e;
+  switch (plan->kernel) {
+    case 1: e = wattn_launch_bf16(plan, q, k, v, o, st, stream); break;
+    case 2: e = wattn_launch_f32x3(plan, q, k, v, o, st, stream); break;
+    case 3: e = wattn_launch_stream(plan, q, k, v, o, st, stream); break;
+    case 4: e = wattn_launch_f32m(plan, q, k, v, o, st, stream); break;
+    case 5: e = wattn_launch_window(plan, q, k, v, o, st, stream); break;
+    default: return SWIN3D_WATTN_EINVAL;  // not a plan of this library
+  }
   return e == 0 ? SWIN3D_WATTN_OK : SWIN3D_WATTN_ELAUNCH;
 }
 

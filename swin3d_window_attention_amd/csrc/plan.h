@@ -14,9 +14,9 @@ struct swin3d_wattn_plan {
   int64_t tokens;           // B * D * H * W
   int64_t elems;            // tokens * heads * head_dim
   int32_t elem_bytes;
-  int32_t kernel;           // 0: f32 VALU, 1: bf16 MFMA (N = 144, dh 64), 2: f32 split-bf16 MFMA,
+  int32_t kernel;           // 1: bf16 MFMA (N = 144, dh 64), 2: f32 split-bf16 MFMA,
                             // 3: bf16 MFMA with K/V streamed (any N, dh 32, 64 or 128),
-                            // 4: f32 MFMA (N <= 144, dh 32 or 64),
+                            // 4: f32 MFMA (N <= 256, dh 32 or 64),
                             // 5: bf16 MFMA, whole window in LDS (N x dh = 144 x 128 or 288 x 64)
   int64_t workgroups;       // workgroups one run launches
   int32_t threads;          // threads per workgroup
@@ -31,13 +31,11 @@ struct swin3d_wattn_plan {
   int32_t special[3][3];
 };
 
-// Kernel launchers, one per source file (wattn_f32.hip, wattn_bf16.hip,
-// wattn_f32x3.hip).
+// Kernel launchers (wattn_bf16.hip, wattn_f32x3.hip, wattn_stream.hip for
+// the streaming and the whole-window kernels, wattn_f32m.hip).
 // Each launches its kernel for the plan on `stream` (a hipStream_t) and
 // returns the HIP runtime's status (0 = success). `stride` holds the token
 // strides of Q, K, V and O in elements, already validated.
-int wattn_launch_f32(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
-                     const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_bf16(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                       const swin3d_wattn_strides_t* stride, void* stream);
 int wattn_launch_f32x3(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,

@@ -80,7 +80,7 @@ __device__ __forceinline__ int k_off(int r, int c) {
 }
 
 template <int DH, int NT, bool kTail>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void wattn_f32m_item(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH, NT>::kBytes > 80 * 1024 ? 1 : 2))) void wattn_f32m_item(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
     const AttnParams p) {
   using L = Lds<DH, NT>;
@@ -129,20 +129,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
     }
   }
-  // lane (kk = g4, query l16) of a tile holds dims kk DH/4 .. + DH/4 - 1
-  floatx4 qf[kMaxQT][kQC];
+  // lane (kk = g4, query l16) of a tile holds dims kk DH/4 .. + DH/4 - 1. Up to
+  // ten tiles, every tile's Q is loaded here; beyond, the first tile's here and
+  // each later one during the tile before it (the compiler may keep that tile
+  // loop rolled, so no register array in it is indexed by the tile)
+  constexpr int kPre = kNT > 10 ? 1 : kMaxQT;
+  auto load_q = [&](int qt, floatx4 (&dst)[kQC]) {
+    int32_t t;
+    uint32_t unused;
+    map_slot<kTail>(p.g, cur, (uint32_t)(qt * 16 + l16), t, unused);
+    const float* base = q + (size_t)t * p.sq + hoff + g4 * (DH / 4);
 #pragma unroll
-  for (int qi = 0; qi < kMaxQT; ++qi) {
-    const int qt = first + kWaves * qi;
-    if (qt < kNT) {
-      int32_t t;
-      uint32_t unused;
-      map_slot<kTail>(p.g, cur, (uint32_t)(qt * 16 + l16), t, unused);
-      const float* base = q + (size_t)t * p.sq + hoff + g4 * (DH / 4);
+    for (int c = 0; c < kQC; ++c) dst[c] = __builtin_bit_cast(floatx4, ldg16(base + 4 * c));
+  };
+  floatx4 qf[kPre][kQC];
 #pragma unroll
-      for (int c = 0; c < kQC; ++c) qf[qi][c] = __builtin_bit_cast(floatx4, ldg16(base + 4 * c));
-    }
-  }
+  for (int qi = 0; qi < kPre; ++qi)
+    if (first + kWaves * qi < kNT) load_q(first + kWaves * qi, qf[qi]);
   // ---- K row-major (swizzled), V transposed into LDS ----
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -166,10 +169,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __syncthreads();
 
   const float c2 = p.c2, bias_s = p.bias_s;
+  floatx4 qn[kQC];  // beyond ten tiles: the next tile's Q, loaded during this one
 #pragma unroll
   for (int qi = 0; qi < kMaxQT; ++qi) {
     const int qt = first + kWaves * qi;
     if (qt >= kNT) break;
+    constexpr bool kRolling = kNT > 10;
+    const int qs = kRolling ? 0 : qi;  // this tile's Q operands: qf[qs]
+    if (kRolling && qi > 0) {
+#pragma unroll
+      for (int c = 0; c < kQC; ++c) qf[0][c] = qn[c];
+    }
+    if (kRolling && qt + kWaves < kNT) load_q(qt + kWaves, qn);
+
 
     // ---- S^T = K Q^T: k-step s = 4 c + e of lane group kk is dim kk DH/4 + s ----
     // with fewer than four key tiles, k-step s accumulates into set s % kAccS,
@@ -180,24 +192,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int a = 0; a < kAccS; ++a)
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt) S2[a][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // beyond ten key tiles the K operands are read a group of tiles at a time
+    // (4 or 7, a divisor of NT: the MFMAs of a group alternate between at least
+    // four independent accumulators)
+    constexpr int kG = kNT <= 10 ? kNT : kNT % 4 == 0 ? 4 : kNT / 2;
+    static_assert(kNT % kG == 0 && (kG >= 4 || kG == kNT), "whole groups of at least four tiles");
 #pragma unroll
-    for (int c = 0; c < kQC; ++c) {
-      floatx4 kf[kNT];
+    for (int c = 0; c < kQC; ++c)
 #pragma unroll
-      for (int kt = 0; kt < kNT; ++kt)
-        kf[kt] = *reinterpret_cast<const floatx4*>(smem + L::kK + k_off<DH>(kt * 16 + l16, g4 * kQC + c));
+      for (int g0 = 0; g0 < kNT; g0 += kG) {
+        floatx4 kf[kG];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int u = 0; u < kG; ++u)
+          if (g0 + u < kNT)
+            kf[u] = *reinterpret_cast<const floatx4*>(smem + L::kK + k_off<DH>((g0 + u) * 16 + l16, g4 * kQC + c));
 #pragma unroll
-        for (int kt = 0; kt < kNT; ++kt) {
-          floatx4& acc = S2[(4 * c + e) % kAccS][kt];
-          float a = kf[kt][e];
-          FM_BEFORE(a);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[qi][c][e], acc, 0, 0, 0);
-          FM_AFTER(acc);
-          FM_PIN_MFMA();
-        }
-    }
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int u = 0; u < kG; ++u)
+            if (g0 + u < kNT) {
+              floatx4& acc = S2[(4 * c + e) % kAccS][g0 + u];
+              float a = kf[u][e];
+              FM_BEFORE(a);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[qs][c][e], acc, 0, 0, 0);
+              FM_AFTER(acc);
+              FM_PIN_MFMA();
+            }
+      }
     floatx4 S[kNT];
 #pragma unroll
     for (int kt = 0; kt < kNT; ++kt) {
@@ -304,21 +325,20 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
 int wattn_launch_f32m(const swin3d_wattn_plan* p, const void* q, const void* k, const void* v, void* o,
                       const swin3d_wattn_strides_t* stride, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the plan admits N <= 144 (NT = ceil(N / 16) tiles of 16 slots) and head_dim 32 or 64
+  // the plan admits N <= 256 and head_dim 32 or 64: NT = ceil(N / 16) tiles of 16 slots, above 10
+  // rounded up to 12, 14 or 16 (the extra slots are padding)
   const int nt = (p->N + 15) / 16;
   const bool d32 = p->desc.head_dim == 32;
   hipError_t e;
-  switch (nt) {
-    case 1: e = d32 ? launch<32, 1>(p, q, k, v, o, stride, s) : launch<64, 1>(p, q, k, v, o, stride, s); break;
-    case 2: e = d32 ? launch<32, 2>(p, q, k, v, o, stride, s) : launch<64, 2>(p, q, k, v, o, stride, s); break;
-    case 3: e = d32 ? launch<32, 3>(p, q, k, v, o, stride, s) : launch<64, 3>(p, q, k, v, o, stride, s); break;
-    case 4: e = d32 ? launch<32, 4>(p, q, k, v, o, stride, s) : launch<64, 4>(p, q, k, v, o, stride, s); break;
-    case 5: e = d32 ? launch<32, 5>(p, q, k, v, o, stride, s) : launch<64, 5>(p, q, k, v, o, stride, s); break;
-    case 6: e = d32 ? launch<32, 6>(p, q, k, v, o, stride, s) : launch<64, 6>(p, q, k, v, o, stride, s); break;
-    case 7: e = d32 ? launch<32, 7>(p, q, k, v, o, stride, s) : launch<64, 7>(p, q, k, v, o, stride, s); break;
-    case 8: e = d32 ? launch<32, 8>(p, q, k, v, o, stride, s) : launch<64, 8>(p, q, k, v, o, stride, s); break;
-    case 9: e = d32 ? launch<32, 9>(p, q, k, v, o, stride, s) : launch<64, 9>(p, q, k, v, o, stride, s); break;
+#define F32M_CASE(n) \
+  case n:            \
+    e = d32 ? launch<32, n>(p, q, k, v, o, stride, s) : launch<64, n>(p, q, k, v, o, stride, s); \
+    break;
+  switch (nt <= 10 ? nt : nt <= 12 ? 12 : nt <= 14 ? 14 : 16) {
+    F32M_CASE(1) F32M_CASE(2) F32M_CASE(3) F32M_CASE(4) F32M_CASE(5) F32M_CASE(6) F32M_CASE(7)
+    F32M_CASE(8) F32M_CASE(9) F32M_CASE(10) F32M_CASE(12) F32M_CASE(14) F32M_CASE(16)
     default: e = hipErrorInvalidValue;
   }
+#undef F32M_CASE
   return (int)e;
 }

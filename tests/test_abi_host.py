@@ -91,6 +91,8 @@ def test_masked_window_count_matches_oracle_labels():
     (dict(window=(4, 8, 12), shift=(1, 3, 3), dtype="f32", head_dim=64), -2),
     (dict(dtype="f32", head_dim=48), -2),
     (dict(B=2, D=4, H=46341, W=46341), -2),
+    (dict(dtype="f32", head_dim=32, window=(2, 8, 10), shift=(0, 0, 0), D=1, H=1, W=1, heads=65536), -2),
+    (dict(dtype="f32", head_dim=64, window=(2, 8, 17), shift=(0, 0, 0)), -2),  # N = 272 > 256
     (dict(D=1, H=1, W=1, heads=65536), -2),
 ])
 def test_create_rejects(kw, code):
@@ -227,14 +229,13 @@ def test_run_strided_rejects_oversized_span():
 
 
 def test_f32_plans():
-    """F32 I/O: windows of up to 144 slots run on the FP32 matrix-core kernel (4), larger ones
-    (up to 256 slots) on the vector-ALU kernel (0)."""
+    """F32 I/O: windows of up to 256 slots run on the FP32 matrix-core kernel (4)."""
     for kw, kern, wg in [(dict(dtype="f32", head_dim=64), 4, 1800 * 8), (dict(dtype="f32", head_dim=32), 4, 1800 * 8),
                          (dict(dtype="f32", head_dim=64, window=(2, 4, 4), shift=(1, 2, 2)), 4, 2 * 45 * 90 * 8),
                          (dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0)), 4, 4 * 180 * 360 * 8),
                          (dict(dtype="f32", head_dim=64, window=(2, 8, 9), shift=(1, 4, 4)), 4, 2 * 23 * 40 * 8),
-                         (dict(dtype="f32", head_dim=64, window=(2, 8, 10), shift=(1, 4, 5)), 0, None),
-                         (dict(dtype="f32", head_dim=32, window=(4, 8, 8), shift=(2, 4, 4)), 0, None)]:
+                         (dict(dtype="f32", head_dim=64, window=(2, 8, 10), shift=(1, 4, 5)), 4, 2 * 23 * 36 * 8),
+                         (dict(dtype="f32", head_dim=32, window=(4, 8, 8), shift=(2, 4, 4)), 4, 1 * 23 * 45 * 8)]:
         rc, h = _create(**kw)
         assert rc == 0, kw
         info = sw.swin3d_wattn_get_info(h)[1]

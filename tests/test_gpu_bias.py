@@ -27,7 +27,7 @@ CASES = [
     ("window_w2x12x12", 1, 4, 13, 25, 2, 64, (2, 12, 12), (1, 6, 6), "bf16", "bf16", 5),
     ("f32_mfma", 1, 4, 13, 25, 2, 64, (2, 6, 12), (1, 3, 6), "f32", "f32", 4),
     ("f32_mfma_w2x4x4", 1, 4, 10, 13, 2, 32, (2, 4, 4), (1, 2, 3), "f32", "f32", 4),
-    ("f32_valu", 1, 4, 13, 25, 2, 32, (2, 8, 10), (1, 4, 5), "f32", "f32", 0),
+    ("f32_mfma_w2x8x10", 1, 4, 13, 25, 2, 32, (2, 8, 10), (1, 4, 5), "f32", "f32", 4),
 ]
 
 

@@ -1,4 +1,4 @@
-"""GPU parity of the exact FP32 matrix-core kernel (plan dtype "f32", windows of up to 144 slots,
+"""GPU parity of the exact FP32 matrix-core kernel (plan dtype "f32", windows of up to 256 slots,
 head_dim 32 or 64) against the fp64 oracle, with the FP32 bar (1e-5 max abs)."""
 import math
 
@@ -41,6 +41,12 @@ OTHER_WINDOWS = [
     datagen.small_workload("f32m_w1x1x3", 1, 2, 3, 7, 2, 32, (1, 1, 3), (0, 0, 1), "f32", 61),           # N = 3
     datagen.small_workload("f32m_w1x1x1", 1, 2, 3, 4, 2, 64, (1, 1, 1), (0, 0, 0), "f32", 62),           # N = 1
     datagen.small_workload("f32m_w3x5x9", 1, 5, 11, 20, 2, 32, (3, 5, 9), (2, 2, 4), "f32", 63),         # N = 135
+    # windows of 145 to 256 slots: 10 tiles, or 12, 14, 16 with the tail as padding
+    datagen.small_workload("f32m_w2x8x10", 1, 4, 13, 25, 2, 64, (2, 8, 10), (1, 4, 5), "f32", 64),       # N = 160
+    datagen.small_workload("f32m_w2x10x10", 1, 3, 17, 23, 2, 32, (2, 10, 10), (1, 5, 5), "f32", 65),     # N = 200
+    datagen.small_workload("f32m_w2x7x15", 1, 4, 15, 29, 2, 64, (2, 7, 15), (1, 3, 7), "f32", 66),       # N = 210
+    datagen.small_workload("f32m_w4x8x8", 1, 5, 17, 9, 2, 64, (4, 8, 8), (2, 4, 4), "f32", 67),          # N = 256
+    datagen.small_workload("f32m_w4x8x8_dh32", 2, 4, 8, 16, 3, 32, (4, 8, 8), (0, 0, 0), "f32", 68),     # N = 256
 ]
 
 

@@ -24,7 +24,7 @@ CASES = [
     ("ragged_f32", 1, 4, 44, 30, 2, 32, (1, 3, 6), "f32", -100.0),
     ("ragged_f32_dh64", 2, 3, 7, 13, 3, 64, (1, 5, 11), "f32", -math.inf),
     ("f32_window_2x4x4", 1, 4, 10, 13, 2, 32, (1, 2, 3), "f32", -100.0, (2, 4, 4)),  # matrix cores, N = 32
-    ("f32_window_2x8x10", 1, 4, 13, 25, 2, 32, (1, 4, 5), "f32", -100.0, (2, 8, 10)),  # vector-ALU kernel, N = 160
+    ("f32_window_2x8x10", 1, 4, 13, 25, 2, 32, (1, 4, 5), "f32", -100.0, (2, 8, 10)),  # matrix cores, N = 160
 ]
 
 
