@@ -117,7 +117,7 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
   if (kernel == 3) {
     // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of
     // 16 slots per wave and query tile, two tiles per wave at head_dim 32 and 64
-    const int64_t qblock = (int64_t)(threads / 64) * 16 * (d.head_dim <= 64 ? 2 : 1);
+    const int64_t qblock = (int64_t)(threads / 64) * 16 * 2;
     const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, qblock);
     if (gx >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
     workgroups = gx * d.heads;

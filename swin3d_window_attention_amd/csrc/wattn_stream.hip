@@ -11,9 +11,9 @@
 // workgroups per CU), and wattn_stream_item streams every other window.
 //
 // wattn_stream_item:
-// Work: one workgroup per (window, head, block of query slots), QT tiles of
-// 16 queries per wave (two at head_dim 32 and 64, where each K and V operand
-// read from LDS serves both, one at head_dim 128); K and V of the window pass
+// Work: one workgroup per (window, head, block of query slots), QT = 2 tiles
+// of 16 queries per wave (each K and V operand read from LDS serves both);
+// K and V of the window pass
 // through LDS in chunks of key slots,
 // double-buffered: while the waves work on chunk c, each thread holds its
 // part of chunk c + 1 in registers and writes it to the other buffer
@@ -118,7 +118,7 @@ __device__ __forceinline__ int v_off(int key, int d) {
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
 template <int DH, int WAVES, int KC, int QT>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? (QT == 1 ? 4 : 3) : KC == 48 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ o, const StreamParams p) {
@@ -785,10 +785,10 @@ int wattn_launch_stream(const swin3d_wattn_plan* p, const void* q, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool k48 = p->threads == 192;  // the plan's block shape: 3 waves and 48-key chunks
   hipError_t e;
-  // head_dim 32 and 64: two query tiles per wave (each K and V operand read
-  // from LDS serves both); head_dim 128: one, within the register budget
+  // two query tiles per wave at every head_dim: each K and V operand read
+  // from LDS serves both
   if (p->desc.head_dim == 128)
-    e = k48 ? launch<128, 3, 48, 1>(p, q, k, v, o, stride, s) : launch<128, 4, 64, 1>(p, q, k, v, o, stride, s);
+    e = k48 ? launch<128, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<128, 4, 64, 2>(p, q, k, v, o, stride, s);
   else if (p->desc.head_dim == 64)
     e = k48 ? launch<64, 3, 48, 2>(p, q, k, v, o, stride, s) : launch<64, 4, 64, 2>(p, q, k, v, o, stride, s);
   else

@@ -122,10 +122,10 @@ def test_window_plans():
 
 def test_streaming_plans():
     """Other bf16 windows, and head_dim 32, go to the K/V-streaming kernel (3): 3 waves and 48-key
-    chunks where N is a multiple of 48 but not of 64, else 4 waves and 64; 16 query slots per wave
-    at head_dim 128, 32 at head_dim 32 and 64."""
+    chunks where N is a multiple of 48 but not of 64, else 4 waves and 64; 32 query slots per wave
+    (two tiles of 16) at every head_dim."""
     for kw, wg, thr in [(dict(window=(2, 6, 6), shift=(1, 3, 3)), 3600 * 1 * 8, 256),     # N = 72: 1 x 128
-                        (dict(window=(3, 12, 12), shift=(1, 6, 6), head_dim=128), 904 * 9 * 8, 192),  # 432: 9 x 48
+                        (dict(window=(3, 12, 12), shift=(1, 6, 6), head_dim=128), 904 * 5 * 8, 192),  # 432: 5 x 96
                         (dict(window=(3, 12, 12), shift=(1, 6, 6)), 904 * 5 * 8, 192),    # N = 432: 5 x 96
                         (dict(window=(4, 12, 24), shift=(2, 6, 12)), 232 * 9 * 8, 256),   # N = 1152 = 9 x 128
                         (dict(window=(1, 7, 7), shift=(0, 3, 3), head_dim=128), 4 * 26 * 52 * 1 * 8, 256),
