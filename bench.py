@@ -316,7 +316,7 @@ def main():
                          "stress_f32_split (FP32 I/O on the split-bf16 matrix-core kernel), "
                          "stage1_f32, stage3_pad_f32, stress_f32 (exact FP32 on the matrix cores), "
                          "stage1_h4d128, stage1_w2x12x12 (whole window in LDS), "
-                         "stage1_w4x12x24 (K/V streamed through LDS), "
+                         "stage1_w4x12x24, stage1_w3x12x12_h4d128 (K/V streamed through LDS), "
                          "adaln_stage1 (the fused AdaLN + residual step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -87,6 +87,8 @@ WORKLOADS = {
     "stage1_w2x12x12": Workload("stage1_w2x12x12", 1, 4, 180, 360, 8, 64, (2, 12, 12), (1, 6, 6), "bf16", 1),
     "stage1_h4d128": Workload("stage1_h4d128", 1, 4, 180, 360, 4, 128, (2, 6, 12), (1, 3, 6), "bf16", 1),
     "stage1_w4x12x24": Workload("stage1_w4x12x24", 1, 4, 180, 360, 8, 64, (4, 12, 24), (2, 6, 12), "bf16", 1),
+    "stage1_w3x12x12_h4d128": Workload("stage1_w3x12x12_h4d128", 1, 4, 180, 360, 4, 128, (3, 12, 12), (1, 6, 6),
+                                       "bf16", 1),
     # FP32-I/O runs of the stage shapes (unrounded float32 draws) for the split-bf16
     # matrix-core path and the exact fp32 path
     "stage1_f32_split": Workload("stage1_f32_split", 1, 4, 180, 360, 8, 64, (2, 6, 12), (1, 3, 6), "f32", 1,

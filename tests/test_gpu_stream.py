@@ -67,10 +67,13 @@ def test_large_logits(wl):
         check(wl, np.stack([o[..., h, :] for h in ref]), np.stack(list(ref.values())), f"bias={bias}")
 
 
-def test_stage1_grid_window_4x12x24_sampled():
+@pytest.mark.parametrize("name", ["stage1_w4x12x24", "stage1_w3x12x12_h4d128"])
+def test_stage1_grid_streaming_sampled(name):
     """The stage-1 grid with window (4, 12, 24) (N = 1152, K and V of 295 KB per window and head:
-    18 chunks) in the launch configuration the benchmark times, on 12 sampled windows."""
-    wl = datagen.WORKLOADS["stage1_w4x12x24"]
+    18 chunks), and with window (3, 12, 12) at 4 heads x 128 (N = 432 in nine 48-key chunks; the
+    depth axis padded from 4 to 6), in the launch configuration the benchmark times, on 12 sampled
+    windows each."""
+    wl = datagen.WORKLOADS[name]
     x = device_inputs(wl, keep_host=True)
     o = run_gpu(wl, -100.0, x)
     assert not torch.isnan(o).any().item()
