@@ -60,3 +60,16 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_help_lists_every_bench_workload():
+    """Every stage, stress and shape workload can be named on the command line and is listed in
+    --help (the tiny case is a smoke and test input only)."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0
+    text = " ".join(r.stdout.split())
+    for name in datagen.WORKLOADS:
+        if name != "tiny_f32":
+            assert name in text, name
+    assert "adaln_stage1" in text
