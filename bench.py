@@ -29,7 +29,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 (matrix)
 KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "wattn_bf16.hip")
+# every input of the headline launch: the kernel, the host code that builds its
+# plan and arguments, the public header, and the build script (compiler flags)
+LAUNCH_INPUTS = [KERNEL_SRC] + [os.path.join(ROOT, *f) for f in (
+    ("swin3d_window_attention_amd", "csrc", "plan.h"),
+    ("swin3d_window_attention_amd", "csrc", "api.cpp"),
+    ("include", "swin3d_wattn.h"),
+    ("swin3d_window_attention_amd", "build.py"))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wattn_bf16_stage1.json")
+# the shapes the pages measure, besides the headline: a tiny FP32 check, the
+# stage-2 shape without and with shift, the padded stage-3 shape and the
+# high-resolution large-logit stress grid
+CONFIG_WORKLOADS = ("tiny_f32", "stage2_s0", "stage2", "stage3_pad", "stress_hres")
 
 
 def log(msg):
@@ -50,8 +61,14 @@ def algorithmic_work(wl):
 
 
 def kernel_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over every input of the headline launch (file names and contents, in order)."""
+    h = hashlib.sha256()
+    for path in LAUNCH_INPUTS:
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -61,7 +78,7 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256") != kernel_digest():
+    if t.get("launch_sha256") != kernel_digest():
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -71,11 +88,71 @@ def _cpu_time():
     return r.ru_utime + r.ru_stime
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_run(task, budget_s: float):
+    """Run task(worker, i) on a pool of threads, one per core this process may use, each
+    worker repeating its tasks until budget_s of wall time has passed since the start (a
+    task in flight at the deadline is finished and counted). BLAS runs one thread per
+    worker. Returns (tasks done per worker, wall seconds, CPU seconds, workers)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover - BLAS then keeps its own threading
+        limit = None
+    try:
+        c0, t0 = _cpu_time(), time.perf_counter()
+
+        def worker(w):
+            done = 0
+            while True:
+                task(w, done)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    return done
+
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            counts = list(ex.map(worker, range(n)))
+        wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return counts, wall, cpu, n
+
+
+def _baseline_record(value, sample, wall, cpu, workers):
+    return {
+        "value": value,
+        "unit": "tokens/s",
+        "cores": max(1, int(round(cpu / wall))),
+        "kind": "oracle",
+        "sample": sample,
+        "cpu_seconds": round(cpu, 2),
+        "workers": workers,
+        "cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+    }
+
+
 def cpu_baseline(wl, budget_s: float, bias: float = -100.0):
     """The fp64 oracle, as it stands, timed on a bounded sample of the same workload for about
-    budget_s of wall time: whole heads of the grid, one call per head (cycling through the heads),
-    where the grid is no larger than the stage-1 one; otherwise seeded batches of 16 random
-    windows, every head, read from the same inputs."""
+    budget_s of wall time, on a thread pool with one worker per available core (BLAS at one
+    thread per worker). Where the grid is no larger than the stage-1 one, each task is one call
+    of the whole-grid oracle on one head (worker w's task i takes head (w + i * workers) mod
+    heads); otherwise each task is a seeded batch of 16 random windows with every head, read
+    from the same inputs."""
     import numpy as np
 
     import datagen
@@ -85,20 +162,20 @@ def cpu_baseline(wl, budget_s: float, bias: float = -100.0):
     nwin = oracle.window_count(wl.B, grid, wl.window)
     if wl.tokens * wl.heads * wl.head_dim <= 259200 * 8 * 64:
         q, k, v = (datagen.full_f64(wl, t) for t in ("q", "k", "v"))
-        done = 0
-        c0, t0 = _cpu_time(), time.perf_counter()
-        while True:
-            h = done % wl.heads
+        workers = len(os.sched_getaffinity(0))
+
+        def task(w, i):
+            h = (w + i * workers) % wl.heads
             sl = (Ellipsis, slice(h, h + 1), slice(None))
             oracle.swin3d_window_attention(q[sl], k[sl], v[sl], wl.window, wl.shift, wl.scale, bias)
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+
+        counts, wall, cpu, n = _pool_run(task, budget_s)
         del q, k, v
+        done = sum(counts)
         frac = done / wl.heads
-        sample = (f"fp64 numpy oracle on the whole {wl.name} grid, one head per call, {done} head pass{'es' if done > 1 else ''} "
-                  f"({done * nwin} window-heads = {frac:.2f} x the workload) in {wall:.1f} s")
+        sample = (f"fp64 numpy oracle on the whole {wl.name} grid, one head per call, {done} head "
+                  f"pass{'es' if done > 1 else ''} ({done * nwin} window-heads = {frac:.2f} x the workload) "
+                  f"on {n} threads in {wall:.1f} s")
     else:
         host = {t: datagen.full_io(wl, t) for t in ("q", "k", "v")}
 
@@ -107,33 +184,27 @@ def cpu_baseline(wl, budget_s: float, bias: float = -100.0):
             return (datagen.bf16_bits_to_f32(a) if wl.dtype == "bf16" else a).astype(np.float64)
 
         nw = [oracle.padded_extent(x, w) // w for x, w in zip(grid, wl.window)]
-        rng = np.random.default_rng(12345)
-        done = 0
-        c0, t0 = _cpu_time(), time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            wins = [(int(rng.integers(wl.B)),) + tuple(int(rng.integers(n)) for n in nw) for _ in range(16)]
+
+        def task(w, i):
+            rng = np.random.default_rng([12345, w, i])
+            wins = [(int(rng.integers(wl.B)),) + tuple(int(rng.integers(m)) for m in nw) for _ in range(16)]
             oracle.windows_attention(fetch, wl.B, grid, wl.heads, wl.head_dim, wl.window, wl.shift, wl.scale,
                                      bias, wins)
-            done += 16
-        wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
+
+        counts, wall, cpu, n = _pool_run(task, budget_s)
         del host
+        done = 16 * sum(counts)
         frac = done / nwin
         sample = (f"fp64 numpy oracle on {done} seeded random windows of the {wl.name} grid, all {wl.heads} "
-                  f"heads ({frac:.4f} x the workload) in {wall:.1f} s")
-    return {
-        "value": wl.tokens * frac / wall,
-        "unit": "tokens/s",
-        "cores": max(1, int(round(cpu / wall))),
-        "kind": "oracle",
-        "sample": sample,
-        "cpu_seconds": round(cpu, 2),
-        "cores_available": len(os.sched_getaffinity(0)),
-    }
+                  f"heads ({frac:.4f} x the workload) on {n} threads in {wall:.1f} s")
+    return _baseline_record(wl.tokens * frac / wall, sample, wall, cpu, n)
 
 
 def cpu_baseline_adaln(wl, a, budget_s: float):
-    """The fp64 AdaLN + residual oracle on consecutive blocks of 4,096 rows of the same inputs
-    (cycling) for about budget_s of wall time."""
+    """The fp64 AdaLN + residual oracle on blocks of 4,096 rows of the same inputs (worker w's
+    task i takes block (w + i * workers), cycling over the rows; the block at the end of the rows
+    is shorter) on a thread pool with one worker per available core, for about budget_s of wall
+    time. Counts the rows actually processed."""
     import numpy as np
 
     import datagen
@@ -142,25 +213,23 @@ def cpu_baseline_adaln(wl, a, budget_s: float):
     def f64(x, dt):
         return (datagen.bf16_bits_to_f32(x) if dt == "bf16" else x).astype(np.float64)
 
-    rows, step, done = wl.rows, 4096, 0
-    c0, t0 = _cpu_time(), time.perf_counter()
-    while time.perf_counter() - t0 < budget_s or done == 0:
-        r = (done * step) % rows
-        sl = slice(r, min(rows, r + step))
+    step = 4096
+    nblocks = -(-wl.rows // step)
+    workers = len(os.sched_getaffinity(0))
+    rows_done = [0] * workers
+
+    def task(w, i):
+        r = ((w + i * workers) % nblocks) * step
+        sl = slice(r, min(wl.rows, r + step))
         oadaln.adaln_residual(f64(a["x"][:, sl], wl.x_dtype), f64(a["res"][:, sl], wl.res_dtype),
                               a["gamma"].astype(np.float64), a["beta"].astype(np.float64), wl.eps)
-        done += 1
-    wall, cpu = time.perf_counter() - t0, _cpu_time() - c0
-    n_rows = done * step * wl.B
-    return {
-        "value": n_rows / wall,
-        "unit": "tokens/s",
-        "cores": max(1, int(round(cpu / wall))),
-        "kind": "oracle",
-        "sample": f"fp64 numpy oracle on {done} blocks of {step} rows x {wl.B} batch of the {wl.name} inputs in {wall:.1f} s",
-        "cpu_seconds": round(cpu, 2),
-        "cores_available": len(os.sched_getaffinity(0)),
-    }
+        rows_done[w] += (sl.stop - sl.start) * wl.B
+
+    counts, wall, cpu, n = _pool_run(task, budget_s)
+    n_rows = sum(rows_done)
+    sample = (f"fp64 numpy oracle on {sum(counts)} blocks of up to {step} rows x {wl.B} batch ({n_rows} rows) "
+              f"of the {wl.name} inputs on {n} threads in {wall:.1f} s")
+    return _baseline_record(n_rows / wall, sample, wall, cpu, n)
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -207,7 +276,8 @@ def write_traffic(prof_dir: str, copy_bytes: int = 536870912):
     and WRITE_SIZE (KiB per dispatch) of the stage-1 kernel, each scaled by what the same counter
     reads for a plain device copy of copy_bytes (subfolders fetch, write, copyfetch, copywrite
     of prof_dir, as written by the commands in profiles/wattn_bf16_item_stage1_hbm_traffic.md).
-    Host only; records the SHA-256 of the kernel source the counters were taken on."""
+    Host only; records the SHA-256 of the launch inputs (kernel source, plan and argument code,
+    header, build flags) the counters were taken on."""
     import csv
     import glob
 
@@ -233,8 +303,8 @@ def write_traffic(prof_dir: str, copy_bytes: int = 536870912):
         "kernel": "wattn_bf16_item",
         "workload": "stage-1 latent grid B=1 D=4 H=180 W=360, 8 heads, head_dim 64, window (2,6,12), "
                     "shift (1,3,6), bf16",
-        "kernel_source": os.path.relpath(KERNEL_SRC, ROOT),
-        "kernel_sha256": kernel_digest(),
+        "launch_inputs": [os.path.relpath(f, ROOT) for f in LAUNCH_INPUTS],
+        "launch_sha256": kernel_digest(),
         "fetch_size_kib_per_dispatch": fetch,
         "write_size_kib_per_dispatch": write,
         "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_size_kib": cfetch,
@@ -303,6 +373,81 @@ def bench_adaln(args):
     }), flush=True)
 
 
+def warm_then_time(torch, run, stream, steps: int, warmup: int, warmup_ms: float):
+    """warmup calls, then more until the GPU has run for warmup_ms (engine clocks ramp up under
+    sustained load; a cold first pass reads about 10% slow), then `steps` back-to-back calls
+    between two HIP events on the launch stream. Returns (ms per call, extra warm-up calls)."""
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    extra = 0
+    while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+        extra += 20
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, extra
+
+
+def roofline_of(wl, ms: float) -> dict:
+    """Position of one launch of workload wl taking ms against the bound of its kernel: HBM bytes
+    at 8 TB/s or products at the matrix-core peak of their own type, whichever takes longer."""
+    nbytes, flops, _ = algorithmic_work(wl)
+    sec = ms / 1e3
+    mfma_peak = F32_MFMA_PEAK_TFLOPS if wl.plan_dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    if flops / (mfma_peak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        a = flops / sec / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": mfma_peak, "unit": "TFLOP/s", "frac": a / mfma_peak}
+    a = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+
+
+def bench_configs(torch, dev, stream, args, names=CONFIG_WORKLOADS) -> dict:
+    """The other measured shapes, each timed like the headline (same warm-up and event protocol,
+    inputs resident on the device, the same bias). Inputs of one shape are freed before the next
+    is generated."""
+    import datagen
+    import swin3d_window_attention_amd as sw
+
+    out = {}
+    for name in names:
+        wl = datagen.WORKLOADS[name]
+        log(f"[bench] config {name}: inputs {wl.shape} {wl.dtype}")
+        x = {t: datagen.to_torch(datagen.full_io(wl, t), wl.dtype).to(dev) for t in ("q", "k", "v")}
+        o = torch.empty_like(x["q"])
+        plan = sw.Plan(*wl.shape, window=wl.window, shift=wl.shift, dtype=wl.plan_dtype, scale=wl.scale,
+                       cross_region_bias=args.bias)
+        info = plan.info()
+        ms, _ = warm_then_time(torch, lambda: plan.run(x["q"], x["k"], x["v"], o), stream, args.steps,
+                               args.warmup, min(args.warmup_ms, 200.0))
+        nbytes, flops, nwin = algorithmic_work(wl)
+        out[name] = {
+            "shape": {"B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
+                      "window": list(wl.window), "shift": list(wl.shift), "dtype": wl.dtype,
+                      "windows": nwin, "masked_windows": info.n_masked_windows, "kernel": info.kernel},
+            "us_per_step": ms * 1e3,
+            "tokens_per_s": wl.tokens / (ms / 1e3),
+            "steps": args.steps,
+            "algorithmic_bytes_per_launch": nbytes,
+            "algorithmic_flops_per_launch": flops,
+            "roofline": roofline_of(wl, ms),
+        }
+        log(f"[bench] config {name}: {ms * 1e3:.1f} us per step, "
+            f"{out[name]['roofline']['frac']:.3f} of the {out[name]['roofline']['bound']} roofline")
+        del x, o, plan
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +465,9 @@ def main():
                          "adaln_stage1 (the fused AdaLN + residual step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="with the headline workload: skip timing the other shapes (" +
+                         ", ".join(CONFIG_WORKLOADS) + ") that the line reports under 'configs'")
     ap.add_argument("--cold", action="store_true",
                     help="flush the 256 MB Infinity Cache (read a 1 GiB buffer) before every timed "
                          "launch and time each launch with its own events")
@@ -366,24 +514,13 @@ def main():
     info = plan.info()
     stream = torch.cuda.current_stream(dev)
 
-    # warm-up: the requested steps, then more until the GPU has run the kernel for
-    # --warmup-ms (engine clocks ramp up under sustained load; a cold first pass
-    # reads about 10% slow)
-    for _ in range(args.warmup):
+    def run():
         plan.run(x["q"], x["k"], x["v"], o)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    extra = 0
-    while (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
-        for _ in range(20):
-            plan.run(x["q"], x["k"], x["v"], o)
-        torch.cuda.synchronize()
-        extra += 20
-    log(f"[bench] warmup {args.warmup} + {extra} steps done; timing {args.steps} steps")
 
     if args.cold:
         # a read-only pass over 1 GiB replaces the cache contents with clean, unrelated lines
         # (a write pass would leave dirty lines that the timed kernel then has to write back)
+        warm_then_time(torch, run, stream, 1, args.warmup, args.warmup_ms)
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         sink = torch.empty((), dtype=torch.float32, device=dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -392,20 +529,14 @@ def main():
         for s, e in evs:
             torch.amax(flush, dim=0, out=sink)
             s.record(stream)
-            plan.run(x["q"], x["k"], x["v"], o)
+            run()
             e.record(stream)
         torch.cuda.synchronize()
         ms = sum(s.elapsed_time(e) for s, e in evs) / args.steps
         del flush
     else:
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(args.steps):
-            plan.run(x["q"], x["k"], x["v"], o)
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
+        ms, extra = warm_then_time(torch, run, stream, args.steps, args.warmup, args.warmup_ms)
+        log(f"[bench] warmup {args.warmup} + {extra} steps done; timed {args.steps} steps")
     log(f"[bench] {ms * 1000:.1f} us per step{' (cold cache)' if args.cold else ''}")
 
     # context, after the timed region: single launches each between their own
@@ -426,6 +557,10 @@ def main():
         plan.run(x["q"], x["k"], x["v"], o)
     pages_mean5 = sum(single_launches(5)) / 5
     copy_gbs = device_copy_gbs(torch, 1 << 29)
+
+    configs = None
+    if headline and not args.no_configs:
+        configs = bench_configs(torch, dev, stream, args)
 
     nbytes, flops, nwin = algorithmic_work(wl)
     sec = ms / 1e3
@@ -492,6 +627,8 @@ def main():
         "algorithmic_flops_per_launch": flops,
         "cpu_baseline": cpu,
     }
+    if configs is not None:
+        line["configs"] = configs
     print(json.dumps(line), flush=True)
 
 

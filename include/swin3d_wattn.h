@@ -86,7 +86,11 @@ typedef struct {
 
 typedef struct swin3d_wattn_plan* swin3d_wattn_t;
 
-/* Validate *desc and build a plan. Host-only: no device is touched.
+/* Validate *desc and build a plan for the operation above: the window,
+ * shift and cross-region bias fields are the parameters of the shifted-window
+ * mask (Flash-Aurora README, "CuTe DSL window attention"), the dtype selects
+ * a precision mode ("Window attention kernels", "Mixed-precision inference").
+ * Host-only: no device is touched.
  * Supported: dtype BF16 with head_dim 32, 64 or 128, any window with
  * wd*wh*ww <= 4096 and heads < 65536 (N = 144 at head_dim 64 runs the
  * single-tile kernel, N x head_dim = 144 x 128 and 288 x 64 a whole-window
@@ -95,13 +99,20 @@ typedef struct swin3d_wattn_plan* swin3d_wattn_t;
  * pages' multi-stage fallback); dtype F32_SPLIT with
  * head_dim 64, wd*wh*ww = 144 and heads < 65536; dtype F32 with head_dim 32
  * or 64, wd*wh*ww <= 256 and heads < 65536 (FP32 matrix cores). B*D*H*W must be < 2^31 and each
- * of D, H, W < 2^24.
+ * of D, H, W < 2^24. A launch counts the work-items of its first grid
+ * dimension in 32 bits, so the windows (times the query blocks per window of
+ * the streaming kernel) times threads_per_workgroup must be < 2^32; only
+ * windows of a few tokens on very large grids reach that (e.g. window
+ * (1, 1, 1) on 4096 x 4097 tokens), and get EUNSUPPORTED.
  * Returns 0 and stores the plan in *out, or EINVAL / EUNSUPPORTED
  * (then *out is set to NULL when out is not NULL). */
 int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn_t* out);
 
 /* O = window_attention(Q, K, V) on `stream` (a hipStream_t; NULL is the
- * default stream) for the device current on the calling thread.
+ * default stream) for the device current on the calling thread: all five
+ * steps of the operation above in one pass, gathering each window straight
+ * from grid layout and scattering O back (Flash-Aurora README, "Kernel fusion
+ * for backbone memory traffic" and "CuTe DSL window attention").
  * q, k, v, o: device pointers to B*D*H*W*heads*head_dim elements of the
  * plan's dtype, 16-byte aligned; o must not overlap q, k or v (q, k, v may
  * alias each other). Every element of o is written exactly once.
@@ -170,7 +181,9 @@ typedef struct {
 int swin3d_adaln_residual(const swin3d_adaln_desc_t* desc, const void* x, const void* res,
                           const float* gamma, const float* beta, void* out, void* stream);
 
-/* Release a plan. NULL is a no-op. Returns 0. */
+/* Release a plan made by swin3d_wattn_create (a host object only: the pages'
+ * kernels hold no state between calls, and neither does a plan on the
+ * device). NULL is a no-op. Returns 0. */
 int swin3d_wattn_destroy(swin3d_wattn_t plan);
 
 /* Static English text for a return code. */

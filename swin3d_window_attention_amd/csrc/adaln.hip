@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 
 struct AdalnParams {
   int32_t rows;   // B * T
+  int32_t row0;   // first row of this launch
   int32_t C;
   int32_t units;  // C / 256: 4-channel units per lane
   FastDiv div_t;  // by T (rows per batch element)
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(64 * kWaves) void adaln_residual_kernel(const XT* _
   constexpr bool kEarly = U <= 4;
   constexpr bool kGuard = U == kMaxUnits;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = p.row0 + (int)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= p.rows) return;  // whole waves only
   const int b = (int)fdiv((uint32_t)row, p.div_t);
   const size_t base = (size_t)row * p.C;
@@ -157,9 +158,17 @@ hipError_t launch_u(const swin3d_adaln_desc_t* d, const void* x, const void* res
   const RT* rr = static_cast<const RT*>(res);
   OT* oo = static_cast<OT*>(out);
   void* args[] = {&xx, &rr, &gamma, &beta, &oo, &p};
-  const unsigned blocks = (unsigned)((p.rows + kWaves - 1) / kWaves);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&adaln_residual_kernel<XT, RT, OT, U>), dim3(blocks),
-                         dim3(64 * kWaves), args, 0, s);
+  // a dispatch counts its work-items in 32 bits: at most kPiece rows (2^30
+  // work-items) per launch, in order on the stream
+  constexpr int32_t kPiece = 1 << 24;
+  for (p.row0 = 0; p.row0 < p.rows; p.row0 += kPiece) {
+    const int32_t n = p.rows - p.row0 < kPiece ? p.rows - p.row0 : kPiece;
+    const unsigned blocks = (unsigned)((n + kWaves - 1) / kWaves);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&adaln_residual_kernel<XT, RT, OT, U>),
+                                         dim3(blocks), dim3(64 * kWaves), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename XT, typename RT, typename OT>

@@ -113,15 +113,18 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   int64_t elems = tokens * d.heads * d.head_dim;
   int64_t n_windows = (int64_t)d.B * nwin[0] * nwin[1] * nwin[2];
-  int64_t workgroups = n_windows * d.heads;
+  // launch grid (gx, heads): gx = windows, or for kernel 3 windows padded to a
+  // multiple of 8 (one XCD per window) x query blocks of 16 slots per wave and
+  // query tile, two tiles per wave
+  int64_t gx = n_windows;
   if (kernel == 3) {
-    // grid: windows padded to a multiple of 8 (one XCD per window) x query blocks of
-    // 16 slots per wave and query tile, two tiles per wave at head_dim 32 and 64
     const int64_t qblock = (int64_t)(threads / 64) * 16 * 2;
-    const int64_t gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, qblock);
-    if (gx >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
-    workgroups = gx * d.heads;
+    gx = ceil_div(n_windows, 8) * 8 * ceil_div(N, qblock);
   }
+  // a dispatch counts its work-items per grid dimension in 32 bits: gx x threads
+  // must stay below 2^32 (reached only by windows of a few tokens on very large grids)
+  if (gx * threads >= (int64_t(1) << 32)) return SWIN3D_WATTN_EUNSUPPORTED;
+  const int64_t workgroups = gx * d.heads;
   if (workgroups >= (int64_t(1) << 31)) return SWIN3D_WATTN_EUNSUPPORTED;
 
   // masked-window count (windows needing the region / padding path)

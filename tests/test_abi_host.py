@@ -254,6 +254,26 @@ def test_grid_extent_limit():
     assert _create(B=1, D=2, H=(1 << 24) + 6, W=12)[0] == -2
 
 
+def test_work_item_limit():
+    """A launch counts the work-items of its first grid dimension in 32 bits: plans whose grid
+    x extent times threads per workgroup reaches 2^32 are refused at create time (EUNSUPPORTED)
+    rather than under-dispatched at run time."""
+    # exact FP32, window (1, 1, 1): one window per token, 256 threads each
+    ok = dict(dtype="f32", head_dim=32, window=(1, 1, 1), shift=(0, 0, 0), heads=1, B=1, D=1)
+    rc, h = _create(H=4096, W=4095, **ok)  # 16,773,120 windows x 256 < 2^32
+    assert rc == 0
+    assert sw.swin3d_wattn_get_info(h)[1].workgroups == 4096 * 4095
+    sw.swin3d_wattn_destroy(h)
+    assert _create(H=4096, W=4097, **ok)[0] == -2   # 16,781,312 x 256 >= 2^32
+    assert _create(H=4096, W=4096, **ok)[0] == -2   # exactly 2^24 windows: 2^32 work-items
+    # bf16 K/V streaming, windows (2, 2, 2) and (1, 2, 2): x extent = windows padded to 8 x 1 query block
+    st = dict(head_dim=64, heads=1, B=1, shift=(0, 0, 0))
+    assert _create(window=(2, 2, 2), D=2, H=4096, W=8190, **st)[0] == 0       # 8,386,560 x 256 < 2^32
+    assert _create(window=(2, 2, 2), D=8, H=8192, W=8192, **st)[0] == -2      # 67M tokens
+    assert _create(window=(1, 2, 2), D=1, H=8192, W=16384, **st)[0] == -2     # 134M tokens
+    assert _create(window=(1, 2, 2), D=1, H=4096, W=16380, **st)[0] == 0      # 16,773,120 windows / 4 x 256
+
+
 def test_strerror():
     assert sw.swin3d_wattn_strerror(0) == "success"
     for c in (-1, -2, -3):

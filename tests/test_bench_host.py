@@ -48,10 +48,26 @@ def test_cpu_baseline_whole_heads(name):
     assert "one head per call" in r["sample"]
 
 
+def test_cpu_baseline_pool():
+    """The oracle baseline runs one worker thread per available core and names the CPU."""
+    r = bench.cpu_baseline(datagen.WORKLOADS["stage3_pad"], 0.05)
+    assert r["workers"] == r["cores_available"] == len(os.sched_getaffinity(0))
+    assert r["cpu_model"] and r["cpu_model"] != "unknown"
+    assert f"on {r['workers']} threads" in r["sample"]
+
+
 def test_cpu_baseline_adaln():
+    """Blocks of 4,096 rows, the last one of the 5,000 rows shorter (904): the rows counted are
+    the rows processed."""
+    import re
+
     wl = datagen.AdalnWorkload("adaln_small", 2, 5000, 256, "bf16", "f32", "f32", 3)
     r = bench.cpu_baseline_adaln(wl, datagen.adaln_inputs(wl), 0.05)
-    assert r["kind"] == "oracle" and r["value"] > 0 and "blocks of 4096 rows" in r["sample"]
+    assert r["kind"] == "oracle" and r["value"] > 0 and "blocks of up to 4096 rows" in r["sample"]
+    m = re.search(r"on (\d+) blocks of up to 4096 rows x 2 batch \((\d+) rows\)", r["sample"])
+    blocks, rows = int(m.group(1)), int(m.group(2))
+    # every block is 4,096 rows or the short last one: rows = 2 (a 4096 + b 904), a + b = blocks
+    assert any(rows == 2 * ((blocks - b) * 4096 + b * 904) for b in range(blocks + 1)), (blocks, rows)
 
 
 def test_more_than_one_gpu_is_refused():

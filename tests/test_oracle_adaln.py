@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.adaln as oadaln
 
 
 def _rand(shape, seed):
@@ -64,22 +65,56 @@ def test_film_and_residual_terms():
                        ref, atol=1e-12)
 
 
-@pytest.mark.parametrize("mutation", ["unbiased", "eps_outside", "no_center", "beta_before_gamma"])
-def test_mutations_are_caught(mutation):
-    """Plausible mistakes in a LayerNorm/FiLM oracle fail the closed forms above."""
+def _mutant_layer_norm(mutation):
     def bad_ln(x, eps):
+        x = np.asarray(x, dtype=np.float64)
         mean = x.mean(axis=-1, keepdims=True)
         if mutation == "unbiased":
             return (x - mean) / np.sqrt(x.var(axis=-1, ddof=1, keepdims=True) + eps)
         if mutation == "eps_outside":
             return (x - mean) / (np.sqrt(x.var(axis=-1, keepdims=True)) + eps)
-        if mutation == "no_center":
-            return x / np.sqrt(x.var(axis=-1, keepdims=True) + eps)
-        return (x - mean) / np.sqrt(x.var(axis=-1, keepdims=True) + eps)
-    C, eps = 256, 0.25
-    x = np.tile([1.0, -1.0], C // 2)[None, None] + (0.5 if mutation == "no_center" else 0.0)
-    expect = (x - x.mean()) / np.sqrt(1.0 + eps)
-    g, b = np.full((1, C), 2.0), np.full((1, C), 0.5)
-    got = bad_ln(x, eps)
-    out = got * g[:, None] + b[:, None] if mutation != "beta_before_gamma" else (got + b[:, None]) * g[:, None]
-    assert not np.allclose(out, expect * g[:, None] + b[:, None], atol=1e-9)
+        assert mutation == "no_center"
+        return x / np.sqrt(x.var(axis=-1, keepdims=True) + eps)
+    return bad_ln
+
+
+def _mutant_adaln(mutation):
+    def bad_adaln(x, res, gamma, beta, eps):
+        xhat = oadaln.layer_norm(x, eps)
+        g = np.asarray(gamma, dtype=np.float64)[:, None, :]
+        b = np.asarray(beta, dtype=np.float64)[:, None, :]
+        r = np.asarray(res, dtype=np.float64)
+        if mutation == "beta_before_gamma":
+            return r + g * (xhat + b)
+        if mutation == "no_residual":
+            return g * xhat + b
+        assert mutation == "gamma_of_batch_0"
+        return r + g[:1] * xhat + b
+    return bad_adaln
+
+
+PINS = [test_layer_norm_matches_torch_layer_norm, test_normalised_rows_have_zero_mean_and_the_closed_form_variance,
+        test_biased_variance_closed_form, test_constant_rows_give_residual_plus_beta,
+        test_shift_and_scale_invariance, test_film_and_residual_terms]
+
+
+@pytest.mark.parametrize("mutation", ["unbiased", "eps_outside", "no_center", "beta_before_gamma", "no_residual",
+                                      "gamma_of_batch_0"])
+def test_mutations_are_caught(mutation, monkeypatch):
+    """A plausible mistake planted in oracle.adaln (in place of its LayerNorm or its FiLM /
+    residual step, also where the package re-exports it) makes at least one pin above fail."""
+    if mutation in ("unbiased", "eps_outside", "no_center"):
+        bad = _mutant_layer_norm(mutation)
+        monkeypatch.setattr(oadaln, "layer_norm", bad)
+        monkeypatch.setattr(oracle, "layer_norm", bad)
+    else:
+        bad = _mutant_adaln(mutation)
+        monkeypatch.setattr(oadaln, "adaln_residual", bad)
+        monkeypatch.setattr(oracle, "adaln_residual", bad)
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the {mutation} mutation"
