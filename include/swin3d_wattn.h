@@ -31,10 +31,11 @@
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
  * computes everything in FP32 (FP32 matrix-core products, FP32 softmax);
  * f32 I/O with F32_SPLIT runs the products as three bf16 matrix-core
- * products each. The kernels fill the padding slots of a window with the
- * nearest real token and give them a zero weight, so Q, K and V must be
- * finite: an Inf or NaN there may also reach the windows that border the
- * padding.
+ * products each. The kernels load the nearest real token into each padding
+ * slot of a window (so every load is unconditional) and replace its K and V
+ * rows by zeros before use, so padding adds exactly nothing: an Inf or NaN in
+ * a real token affects only the outputs of its own window, as in a
+ * materialised pad-shift-partition pipeline.
  *
  * Ownership: the caller owns every device buffer. The library allocates no
  * device memory; a plan is a small immutable host object.

@@ -266,8 +266,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // ---- gather first: each thread maps the slots it loads itself, so the
   // loads leave before any table or barrier. K and V rows go to registers
   // (then LDS), the Q operands of this wave's tiles stay in registers.
-  // Padding slots read their stand-in token: a padding key gets a zero weight
-  // and a padding query is never written, so any finite value will do. ----
+  // Padding slots read their stand-in token (so every load is unconditional)
+  // and their K and V rows are replaced by zeros before they reach LDS: a
+  // padding key then gets an exactly zero weight and adds exactly zero
+  // whatever the stand-in holds (an Inf or NaN there stays in its own
+  // window); a padding query is never written. ----
   constexpr int kChunks = kN * 8;
   constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
   u32x4 kr[kPer], vr[kPer];
@@ -281,6 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // Q rows of this wave's tiles are read whole: load s of a tile covers its
   // rows 8 s .. 8 s + 7, lane L reading 16-byte chunk L % 8 of row 8 s + L / 8
   u32x4 qr[kMaxQT][2];
+  uint32_t padk = 0;  // bit j: load j of this thread is a padding slot's stand-in
   auto gather = [&](auto edge) {
     constexpr bool kEdge = decltype(edge)::value;
 #pragma unroll
@@ -288,10 +292,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int c = tid + kThreads * j;
       if (c < kChunks) {
         int32_t t;
-        uint32_t unused;
-        map_slot<kEdge>(p, cur, (uint32_t)(c >> 3), t, unused);
+        uint32_t code;
+        map_slot<kEdge>(p, cur, (uint32_t)(c >> 3), t, code);
         kr[j] = ldg16(kcol + row_off(t, p.sk));
         vr[j] = ldg16(vcol + row_off(t, p.sv));
+        if (kEdge) padk |= code == kPadSlot ? 1u << j : 0u;
       }
     }
 #pragma unroll
@@ -314,6 +319,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   else
     gather(std::false_type{});
 
+  if (cur.masked) {  // wave-uniform: only windows with a cut or padding hold padding slots
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;

@@ -117,16 +117,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
 
   // ---- gather: K and V rows whole (kCh lanes x 16 B per row), each thread
   // mapping the slots it loads; Q straight into the B-operand layout ----
+  // Padding slots load a stand-in token; their K and V rows are replaced by
+  // zeros before they reach LDS, so the stand-in's values never reach an
+  // output (an Inf or NaN in it stays in its own window).
   u32x4 kr[kPer], vr[kPer];
+  uint32_t padk = 0;  // bit j: load j is a padding slot's stand-in
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;
     if (c < kChunks) {
       int32_t t;
-      uint32_t unused;
-      map_slot<kTail>(p.g, cur, (uint32_t)(c / kCh), t, unused);
+      uint32_t code;
+      map_slot<kTail>(p.g, cur, (uint32_t)(c / kCh), t, code);
       kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c % kCh));
       vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
+      padk |= code == kPadSlot ? 1u << j : 0u;
     }
   }
   // lane (kk = g4, query l16) of a tile holds dims kk DH/4 .. + DH/4 - 1. Up to
@@ -147,6 +152,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   for (int qi = 0; qi < kPre; ++qi)
     if (first + kWaves * qi < kNT) load_q(first + kWaves * qi, qf[qi]);
   // ---- K row-major (swizzled), V transposed into LDS ----
+  if (masked) {  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;

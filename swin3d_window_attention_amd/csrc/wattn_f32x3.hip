@@ -116,15 +116,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int kChunks = kN * 16;
   constexpr int kPer = kChunks / kThreads;
   static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+  // Padding slots load a stand-in token; their K and V rows are replaced by
+  // zeros before they reach LDS, so the stand-in's values never reach an
+  // output (an Inf or NaN in it stays in its own window).
   u32x4 kr[kPer], vr[kPer];
+  uint32_t padk = 0;  // bit j: load j is a padding slot's stand-in
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;
     int32_t t;
-    uint32_t unused;
-    map_slot<false>(p.g, cur, (uint32_t)(c >> 4), t, unused);
+    uint32_t code;
+    map_slot<false>(p.g, cur, (uint32_t)(c >> 4), t, code);
     kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c & 15));
     vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c & 15));
+    padk |= code == kPadSlot ? 1u << j : 0u;
   }
   // Q straight into the operand layout: lane (g4, query l16) of a tile holds
   // dims [8 g4, 8 g4 + 8) and the same + 32 of its query row
@@ -145,6 +150,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // ---- K and V into LDS as hi / lo bf16 tiles: fp32 chunk `part` (dims
   // 4 part .. 4 part + 3) is one 8-byte half of bf16 chunk part / 2 ----
+  if (cur.masked) {  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;

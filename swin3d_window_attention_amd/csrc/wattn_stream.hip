@@ -183,19 +183,37 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   const int my_row = tid / kCh, my_ch = tid % kCh;
   const uint16_t* kcol = k + hoff + 8 * my_ch;
   const uint16_t* vcol = v + hoff + 8 * my_ch;
+  // Padding slots (and slots past N) load a stand-in token; their K and V rows
+  // are replaced by zeros before they reach LDS, so the stand-in's values never
+  // reach an output (an Inf or NaN in it stays in its own window). Ring entries
+  // carry that flag in bit 31 (tokens are below 2^31).
+  uint32_t padk = 0;  // bit i: load i of the chunk in flight is a padding slot's stand-in
   auto fetch = [&](int c) {
+    padk = 0;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int r = my_row + (kThreads / kCh) * i;
       int32_t t;
       if (c == 0) {
-        uint32_t unused;
-        map_slot(p.g, cur, (uint32_t)r, t, unused);
+        uint32_t code;
+        map_slot(p.g, cur, (uint32_t)r, t, code);
+        padk |= code == kPadSlot ? 1u << i : 0u;
       } else {
         t = tok_ring[(c % kRing) * kKC + r];
+        padk |= t < 0 ? 1u << i : 0u;
+        t &= 0x7FFFFFFF;
       }
       kr[i] = ldg16(kcol + row_at(t, p.sk));
       vr[i] = ldg16(vcol + row_at(t, p.sv));
+    }
+  };
+  // zero the stand-in rows of chunk c (wave-uniform: only chunks of a window
+  // with a cut or padding, or running past N, hold padding slots)
+  auto clear_pad = [&](int c) {
+    if (cur.masked || (c + 1) * kKC > p.g.N) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        if (padk & (1u << i)) kr[i] = vr[i] = u32x4{0, 0, 0, 0};
     }
   };
   // tokens and region codes of chunks c0 .. c0 + 3 (those that exist) into the ring
@@ -205,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       int32_t t;
       uint32_t code;
       map_slot(p.g, cur, (uint32_t)(c * kKC + r), t, code);
-      tok_ring[(c % kRing) * kKC + r] = t;
+      tok_ring[(c % kRing) * kKC + r] = code == kPadSlot ? (int32_t)((uint32_t)t | 0x80000000u) : t;
       code_ring[(c % kRing) * kKC + r] = (uint8_t)code;
     }
   };
@@ -240,6 +258,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   }
   // chunk 0 into buffer 0
   fetch(0);
+  clear_pad(0);
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = my_row + (kThreads / kCh) * i;
@@ -424,6 +443,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     // the last reader of that buffer, at the previous barrier) ----
     if (more) {
       uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
+      clear_pad(c + 1);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int r = my_row + (kThreads / kCh) * i;
@@ -516,6 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const int my_row = tid / kCh, my_ch = tid % kCh;
   const uint16_t* kcol = k + hoff + 8 * my_ch;
   const uint16_t* vcol = v + hoff + 8 * my_ch;
+  uint32_t padk = 0;  // bit j: load j of this thread is a padding slot's stand-in
   auto gather = [&](auto edge) {
     constexpr bool kEdge = decltype(edge)::value;
 #pragma unroll
@@ -524,8 +545,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       if (r < kN) {
         int32_t t;
         if (kEdge) {
-          uint32_t unused;
-          map_slot(p.g, cur, (uint32_t)r, t, unused);
+          uint32_t code;
+          map_slot(p.g, cur, (uint32_t)r, t, code);
+          padk |= code == kPadSlot ? 1u << j : 0u;
         } else {
           t = map_slot_plain(p.g, cur, (uint32_t)r);
         }
@@ -554,6 +576,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     gather(std::true_type{});
   else
     gather(std::false_type{});
+  // padding slots: zero K and V rows in LDS, so the stand-in's values never
+  // reach an output (an Inf or NaN in it stays in its own window)
+  if (cur.masked) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int r = my_row + (kThreads / kCh) * j;
