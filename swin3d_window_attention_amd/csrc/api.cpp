@@ -129,7 +129,7 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
 
   // masked-window count (windows needing the region / padding path)
   int64_t masked = 0;
-  int32_t special[3][3];
+  int32_t special[3][3], padwin[3][2];
   bool bad_special = false;
   {
     bool* flags[3][2];
@@ -146,8 +146,9 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     int64_t plain[3];
     for (int a = 0; a < 3; ++a) {
       plain[a] = 0;
-      int ns = 0;
+      int ns = 0, np = 0;
       for (int j = 0; j < 3; ++j) special[a][j] = -1;
+      for (int j = 0; j < 2; ++j) padwin[a][j] = -1;
       for (int32_t i = 0; i < nwin[a]; ++i) {
         if (!flags[a][0][i] && !flags[a][1][i]) {
           ++plain[a];
@@ -155,6 +156,12 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
           special[a][ns++] = i;
         } else {
           bad_special = true;  // cannot happen: padding spans < one window, plus the last window
+        }
+        if (flags[a][1][i]) {
+          if (np < 2)
+            padwin[a][np++] = i;
+          else
+            bad_special = true;  // cannot happen: padding spans fewer positions than a window
         }
       }
     }
@@ -192,8 +199,10 @@ extern "C" int swin3d_wattn_create(const swin3d_wattn_desc_t* desc, swin3d_wattn
     rest -= bf16_value(p->beta_bf16[t]);
   }
   p->pad_bf16 = bf16_rne(big);
-  for (int a = 0; a < 3; ++a)
+  for (int a = 0; a < 3; ++a) {
     for (int j = 0; j < 3; ++j) p->special[a][j] = special[a][j];
+    for (int j = 0; j < 2; ++j) p->padwin[a][j] = padwin[a][j];
+  }
   *out = p;
   return SWIN3D_WATTN_OK;
 }

@@ -29,6 +29,9 @@ struct swin3d_wattn_plan {
   uint16_t pad_bf16;
   // per axis: window indices that hold a region cut or padding (-1 = none)
   int32_t special[3][3];
+  // per axis: window indices that hold padding (-1 = none); padding spans
+  // fewer positions than a window, so at most two windows per axis
+  int32_t padwin[3][2];
 };
 
 // Kernel launchers (wattn_bf16.hip, wattn_f32x3.hip, wattn_stream.hip for

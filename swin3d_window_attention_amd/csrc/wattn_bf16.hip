@@ -119,6 +119,7 @@ __device__ __forceinline__ uint32_t fdiv_small(uint32_t n, uint32_t mul) { retur
 struct AttnParams {
   int32_t X[3], P[3], shift[3], win[3], nwin[3];
   int32_t special[3][3];
+  int32_t padwin[3][2];  // windows that hold padding along each axis (-1 = none)
   FastDiv div_b, div_d, div_h;  // by windows per batch, per depth slab, per row
   uint32_t div_hw, div_w;       // fdiv_small multipliers by wh * ww and by ww
   uint32_t whw;                 // wh * ww
@@ -153,6 +154,7 @@ struct WinPos {
   uint32_t tokb;  // first token of batch element b
   uint32_t tok0;  // token of slot 0 when the window has no cut and no padding
   bool masked;
+  bool padded;    // the window holds padding slots
 };
 
 // Window w (batch folded in) -> (b, kd, kh, kw) and whether it needs the
@@ -174,6 +176,12 @@ __device__ __forceinline__ WinPos decode_window(const AttnParams& p, uint32_t w)
 #pragma unroll
     for (int j = 0; j < 3; ++j) m |= p.special[a][j] == it.k[a];
   it.masked = m;
+  bool pd = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pd |= p.padwin[a][j] == it.k[a];
+  it.padded = pd;
   // without a cut or padding on any axis no slot wraps or falls outside the
   // grid, so slot (od, oh, ow) is token tok0 + od H W + oh W + ow
   it.tok0 = it.tokb + (uint32_t)(it.base[0] + p.shift[0]) * p.plane +
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   else
     gather(std::false_type{});
 
-  if (cur.masked) {  // wave-uniform: only windows with a cut or padding hold padding slots
+  if (cur.padded) {  // wave-uniform
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};
@@ -547,6 +555,7 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
     p.win[a] = d.window[a];
     p.nwin[a] = pl->nwin[a];
     for (int j = 0; j < 3; ++j) p.special[a][j] = pl->special[a][j];
+    for (int j = 0; j < 2; ++j) p.padwin[a][j] = pl->padwin[a][j];
   }
   p.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
   p.div_d = make_fastdiv((uint32_t)(pl->nwin[1] * pl->nwin[2]));

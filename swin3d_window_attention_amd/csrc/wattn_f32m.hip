@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   for (int qi = 0; qi < kPre; ++qi)
     if (first + kWaves * qi < kNT) load_q(first + kWaves * qi, qf[qi]);
   // ---- K row-major (swizzled), V transposed into LDS ----
-  if (masked) {  // wave-uniform
+  if (cur.padded || kTail) {  // wave-uniform: padding slots, or slots past N in the last tile
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};

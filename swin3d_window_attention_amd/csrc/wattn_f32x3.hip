@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // ---- K and V into LDS as hi / lo bf16 tiles: fp32 chunk `part` (dims
   // 4 part .. 4 part + 3) is one 8-byte half of bf16 chunk part / 2 ----
-  if (cur.masked) {  // wave-uniform
+  if (cur.padded) {  // wave-uniform
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};

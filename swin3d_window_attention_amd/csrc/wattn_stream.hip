@@ -203,14 +203,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         padk |= t < 0 ? 1u << i : 0u;
         t &= 0x7FFFFFFF;
       }
-      kr[i] = ldg16(kcol + row_at(t, p.sk));
-      vr[i] = ldg16(vcol + row_at(t, p.sv));
+      // ordinary (not non-temporal) loads: the query blocks of a window read
+      // the same K and V rows one after another on one XCD, from its L2
+      kr[i] = *reinterpret_cast<const u32x4*>(kcol + row_at(t, p.sk));
+      vr[i] = *reinterpret_cast<const u32x4*>(vcol + row_at(t, p.sv));
     }
   };
   // zero the stand-in rows of chunk c (wave-uniform: only chunks of a window
   // with a cut or padding, or running past N, hold padding slots)
   auto clear_pad = [&](int c) {
-    if (cur.masked || (c + 1) * kKC > p.g.N) {
+    if (cur.padded || (c + 1) * kKC > p.g.N) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i)
         if (padk & (1u << i)) kr[i] = vr[i] = u32x4{0, 0, 0, 0};
@@ -283,8 +285,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   }
   const int e = l16 >> 2, qd = l16 & 3;
   const int x32 = (lane ^ 32) << 2;
-  const u32x4 kOnes8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
-  const u32x2 kOnes4 = u32x2{0x3F803F80u, 0x3F803F80u};
+  // bf16 1.0 x 8 / x 4, the A operand of the row-sum products: one register
+  // set for the whole loop (the empty asm before each use pins the order)
+  u32x4 ones8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  u32x2 ones4 = u32x2{0x3F803F80u, 0x3F803F80u};
 
   for (int c = 0; c < p.nchunk; ++c) {
     const int buf = c & 1;
@@ -352,16 +356,23 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       floatx4 S[kKT];
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
-      float mc = S[0][0];
+      // the chunk max, taken from the reference m on (the growth test below
+      // compares with m anyway); NaN-propagating maxima need no quieting of
+      // their inputs, which saves an instruction per operand the compiler
+      // cannot prove canonical
+      float mc = m[u];
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mc = fmaxf(mc, S[kt][i]);
+        for (int i = 0; i < 4; ++i) mc = __builtin_elementwise_maximum(mc, S[kt][i]);
       // the reference max of a row moves only when the chunk's max exceeds it
       // by more than kLazy in the exponent (always on the first chunk, where
       // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
       // does not depend on the reference
-      const float mc_w = wave_max16x4(mc, x32);
+      mc = __builtin_elementwise_maximum(
+          mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc), 0x401F)));
+      const float mc_w = __builtin_elementwise_maximum(
+          mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc))));
       const bool grow = (mc_w - m[u]) * c2 > kLazy;
       const float m_new = grow ? mc_w : m[u];
       const float nm = -m_new * c2;
@@ -407,9 +418,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         }
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        u32x4 ones = kOnes8;
-        ST_BEFORE(ones);
-        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[u][j], Ls[u], 0, 0, 0);
+        ST_BEFORE(ones8);
+        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[u][j], Ls[u], 0, 0, 0);
         ST_AFTER(Ls[u]);
         ST_PIN_MFMA();
       }
@@ -431,9 +441,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         }
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        u32x2 ones = kOnes4;
-        ST_BEFORE(ones);
-        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
+        ST_BEFORE(ones4);
+        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
         ST_AFTER(Ls[u]);
         ST_PIN_MFMA();
       }
@@ -578,7 +587,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     gather(std::false_type{});
   // padding slots: zero K and V rows in LDS, so the stand-in's values never
   // reach an output (an Inf or NaN in it stays in its own window)
-  if (cur.masked) {
+  if (cur.padded) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (padk & (1u << j)) kr[j] = vr[j] = u32x4{0, 0, 0, 0};

@@ -44,6 +44,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 struct Geom {
   int32_t X[3], P[3], shift[3], win[3], nwin[3];
   int32_t special[3][3];
+  int32_t padwin[3][2];         // windows that hold padding along each axis (-1 = none)
   int32_t N;                    // slots per window
   FastDiv div_b, div_d, div_h;  // by windows per batch element, per depth slab, per row
   FastDiv div_hw, div_w;        // by window slots per depth step, per row
@@ -61,6 +62,7 @@ inline Geom make_geom(const swin3d_wattn_plan* pl) {
     g.win[a] = d.window[a];
     g.nwin[a] = pl->nwin[a];
     for (int j = 0; j < 3; ++j) g.special[a][j] = pl->special[a][j];
+    for (int j = 0; j < 2; ++j) g.padwin[a][j] = pl->padwin[a][j];
   }
   g.N = pl->N;
   g.div_b = make_fastdiv((uint32_t)(pl->nwin[0] * pl->nwin[1] * pl->nwin[2]));
@@ -75,6 +77,7 @@ struct WinPos {
   int b, k[3];
   uint32_t tok0;  // token of slot 0 when the window has no cut and no padding
   bool masked;    // the window has a region cut or padding along some axis
+  bool padded;    // the window holds padding slots
 };
 
 // Window w (batch folded in) -> (b, kd, kh, kw)
@@ -93,6 +96,12 @@ __device__ __forceinline__ WinPos decode_window(const Geom& g, uint32_t w) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) m |= g.special[a][j] == it.k[a];
   it.masked = m;
+  bool pd = false;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pd |= g.padwin[a][j] == it.k[a];
+  it.padded = pd;
   // without a cut or padding no slot wraps or falls outside the grid: slot
   // (od, oh, ow) is token tok0 + (od H + oh) W + ow
   it.tok0 = (((uint32_t)it.b * (uint32_t)g.X[0] + (uint32_t)(it.k[0] * g.win[0] + g.shift[0])) * (uint32_t)g.X[1] +
