@@ -642,6 +642,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const uint8_t* vb = smem + L::kTensor;
   const int e = l16 >> 2, qd = l16 & 3;
   const bool odd = g4 & 1;
+  // bf16 1.0 x 8 / x 4, the A operand of the row-sum products: one register
+  // set for all tiles (the empty asm before each use pins the order)
+  u32x4 ones8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  u32x2 ones4 = u32x2{0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int i = 0; i < kMaxQT; ++i) {
     const int qt = wave + kWaves * i;
@@ -685,13 +689,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       }
     }
 
-    // ---- softmax in FP32 (log2 domain), P to bf16 in the B-operand layout ----
+    // ---- softmax in FP32 (log2 domain), P to bf16 in the B-operand layout;
+    // NaN-propagating maxima need no quieting of their inputs ----
     float mx = S[0][0];
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kt][r]);
-    const float nm = -wave_max16x4(mx, x32) * c2;
+      for (int r = 0; r < 4; ++r) mx = __builtin_elementwise_maximum(mx, S[kt][r]);
+    mx = __builtin_elementwise_maximum(
+        mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
+    mx = __builtin_elementwise_maximum(
+        mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mx))));
+    const float nm = -mx * c2;
     bf16x8_t Pb[kJ > 0 ? kJ : 1];
     bf16x4_t Pt, prev;
 #pragma unroll
@@ -732,9 +741,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
         ST_PIN_MFMA_LDS();
       }
-      u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-      ST_BEFORE(ones);
-      Ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), Pb[j], Ls, 0, 0, 0);
+      ST_BEFORE(ones8);
+      Ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[j], Ls, 0, 0, 0);
       ST_AFTER(Ls);
       ST_PIN_MFMA_LDS();
     }
@@ -747,9 +755,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
         ST_PIN_MFMA();
       }
-      u32x2 ones = u32x2{0x3F803F80u, 0x3F803F80u};
-      ST_BEFORE(ones);
-      Ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones), __builtin_bit_cast(short4_t, Pt), Ls, 0, 0, 0);
+      ST_BEFORE(ones4);
+      Ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt), Ls, 0, 0, 0);
       ST_AFTER(Ls);
       ST_PIN_MFMA();
     }
