@@ -230,13 +230,20 @@ __device__ __forceinline__ void map_slot(const AttnParams& p, const WinPos& it, 
 // added to a per-lane column pointer, one 32 x 32 + 64-bit multiply-add
 __device__ __forceinline__ size_t row_off(int32_t t, uint32_t s) { return (uint64_t)(uint32_t)t * s; }
 
-// Q, K and V rows are read exactly once: a non-temporal load marks the
-// line as streaming, so it does not displace useful lines in L2 or the
-// Infinity Cache. Measured on MI355X for this gather pattern: 5.9 TB/s with
-// non-temporal loads against 5.0 TB/s with ordinary ones (output stores stay
-// ordinary: non-temporal stores were slower).
+// Q, K and V rows are read exactly once per launch. Where Q, K and V together
+// exceed the 256 MB Infinity Cache, a non-temporal load marks each line as
+// streaming, so it does not displace useful lines in L2 or that cache
+// (measured on MI355X for this gather pattern: 5.9 TB/s with non-temporal
+// loads against 5.0 TB/s with ordinary ones). Inputs that fit in the cache
+// are read with ordinary loads (kKeep): a launch then finds them there when
+// their producer, or the previous launch on the same inputs, left them
+// there. Output stores stay ordinary (non-temporal stores were slower).
+template <bool kKeep>
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  if constexpr (kKeep)
+    return *reinterpret_cast<const u32x4*>(ptr);
+  else
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
 }
 
 __device__ __forceinline__ short4_t lds_tr(const uint8_t* smem, int byte_off) {
@@ -252,6 +259,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+template <bool kKeep>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void wattn_bf16_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const AttnParams p) {
@@ -302,8 +310,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         int32_t t;
         uint32_t code;
         map_slot<kEdge>(p, cur, (uint32_t)(c >> 3), t, code);
-        kr[j] = ldg16(kcol + row_off(t, p.sk));
-        vr[j] = ldg16(vcol + row_off(t, p.sv));
+        kr[j] = ldg16<kKeep>(kcol + row_off(t, p.sk));
+        vr[j] = ldg16<kKeep>(vcol + row_off(t, p.sv));
         if (kEdge) padk |= code == kPadSlot ? 1u << j : 0u;
       }
     }
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           int32_t t;
           uint32_t unused;
           map_slot<kEdge>(p, cur, (uint32_t)(qt * 16 + 8 * s + (lane >> 3)), t, unused);
-          qr[qi][s] = ldg16(qcol + row_off(t, p.sq));
+          qr[qi][s] = ldg16<kKeep>(qcol + row_off(t, p.sq));
         }
       }
     }
@@ -577,7 +585,10 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_bf16_item),
+  // ordinary loads where Q, K and V together fit in the 256 MB Infinity Cache
+  const bool keep = 3 * pl->elems * pl->elem_bytes <= (int64_t(256) << 20);
+  return hipLaunchKernel(keep ? reinterpret_cast<const void*>(&wattn_bf16_item<true>)
+                              : reinterpret_cast<const void*>(&wattn_bf16_item<false>),
                          dim3((unsigned)pl->n_windows, (unsigned)d.heads), dim3(kThreads), args, 0, s);
 }
 
