@@ -120,18 +120,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   // Padding slots load a stand-in token; their K and V rows are replaced by
   // zeros before they reach LDS, so the stand-in's values never reach an
   // output (an Inf or NaN in it stays in its own window).
+  // The kCh lanes that load one row share its slot map: lane (chunk) ch maps
+  // the row of load ch and writes the slot table entry (token, region code)
+  // of that row; every lane takes the token of its load j from lane j of its
+  // group by a permute, bit 31 flagging a padding slot.
+  static_assert((kCh == 8 || kCh == 16) && kPer <= kCh, "row groups inside one wave, one row per lane");
   u32x4 kr[kPer], vr[kPer];
   uint32_t padk = 0;  // bit j: load j is a padding slot's stand-in
+  const int gbase = (lane & ~(kCh - 1)) * 4;  // byte address of the group's first lane
+  int32_t mtok = 0;
+  {
+    const int r = tid / kCh + (kThreads / kCh) * (tid % kCh);
+    if (tid % kCh < kPer && r < kN) {
+      int32_t t;
+      uint32_t code;
+      map_slot<kTail>(p.g, cur, (uint32_t)r, t, code);
+      tokS[r] = t;
+      codeS[r] = (uint8_t)code;
+      mtok = code == kPadSlot ? (int32_t)((uint32_t)t | 0x80000000u) : t;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;
     if (c < kChunks) {
-      int32_t t;
-      uint32_t code;
-      map_slot<kTail>(p.g, cur, (uint32_t)(c / kCh), t, code);
+      int32_t t = __builtin_amdgcn_ds_bpermute(gbase + 4 * j, mtok);
+      padk |= t < 0 ? 1u << j : 0u;
+      t &= 0x7FFFFFFF;
       kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c % kCh));
       vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c % kCh));
-      padk |= code == kPadSlot ? 1u << j : 0u;
     }
   }
   // lane (kk = g4, query l16) of a tile holds dims kk DH/4 .. + DH/4 - 1. Up to
@@ -168,14 +185,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
       for (int e = 0; e < 4; ++e) vt[(4 * ch + e) * kVtPitch + r] = x[e];
     }
   }
-  // ---- slot table (token, region code) for the mask and the scatter ----
-  for (int r = tid; r < kN; r += kThreads) {
-    int32_t t;
-    uint32_t c;
-    map_slot<kTail>(p.g, cur, (uint32_t)r, t, c);
-    tokS[r] = t;
-    codeS[r] = (uint8_t)c;
-  }
+  // (the slot table for the mask and the scatter was written during the gather)
   __syncthreads();
 
   const float c2 = p.c2, bias_s = p.bias_s;

@@ -160,13 +160,20 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   int32_t qtok[QT];
   uint32_t qcode[QT];
   bf16x8_t qop[QT][kS];
+  bool any_real = false;
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const int qslot = qb * kQB + (wave * QT + u) * 16 + l16;
     map_slot(p.g, cur, (uint32_t)qslot, qtok[u], qcode[u]);
+    any_real |= qcode[u] != kPadSlot;
 #pragma unroll
     for (int s = 0; s < kS; ++s)
       qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
+  }
+  // a block whose query slots are all padding writes nothing: it ends here
+  // (in windows that hold padding only: a wave-uniform test)
+  if (cur.padded || (qb + 1) * kQB > p.g.N) {
+    if (!__syncthreads_or(any_real)) return;
   }
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
@@ -302,149 +309,161 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     // c - 1) finished before the previous barrier
     if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
 
-    // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
-    // for the wave's QT query tiles. Consecutive MFMAs take independent
-    // accumulators: with fewer than four per k-step, even and odd k-steps
-    // accumulate separately, so that no MFMA takes its accumulator from one
-    // of the three before it ----
-    constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
-    floatx4 S2[kAcc][QT][kKT];
+    // ---- a chunk of padding keys only (in a window that holds padding, or
+    // past N) adds nothing: their weights are exactly zero, so it is skipped
+    // (wave-uniform: every wave reads the same codes) ----
+    bool skip = false;
+    if (cur.padded || (c + 1) * kKC > p.g.N) {
+      bool kp = true;
 #pragma unroll
-    for (int a = 0; a < kAcc; ++a)
-#pragma unroll
-      for (int u = 0; u < QT; ++u)
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) S2[a][u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      bf16x8_t kf[kKT];
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-        kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-        for (int u = 0; u < QT; ++u) {
-          ST_BEFORE(kf[kt]);
-          S2[s % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[u][s], S2[s % kAcc][u][kt], 0, 0, 0);
-          ST_AFTER(S2[s % kAcc][u][kt]);
-          ST_PIN_MFMA();
-        }
+      for (int kt = 0; kt < kKT; ++kt) kp = kp && cb[kt * 16 + l16] == kPadSlot;
+      skip = __all(kp);
     }
-    // mask k-step: the window has a cut or padding, or this chunk runs past N
-    if (cur.masked || (c + 1) * kKC > p.g.N) {
-      bf16x8_t xf[kKT];
+    if (!skip) {
+      // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
+      // for the wave's QT query tiles. Consecutive MFMAs take independent
+      // accumulators: with fewer than four per k-step, even and odd k-steps
+      // accumulate separately, so that no MFMA takes its accumulator from one
+      // of the three before it ----
+      constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
+      floatx4 S2[kAcc][QT][kKT];
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-        xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
+      for (int a = 0; a < kAcc; ++a)
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+        for (int u = 0; u < QT; ++u)
 #pragma unroll
-        for (int u = 0; u < QT; ++u) {
-          ST_BEFORE(xf[kt]);
-          S2[kS % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb[u], S2[kS % kAcc][u][kt], 0, 0, 0);
-          ST_AFTER(S2[kS % kAcc][u][kt]);
-          ST_PIN_MFMA();
-        }
-    }
-
-    // ---- online softmax, per query tile ----
-    bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
-    bf16x4_t Pt[QT];
+          for (int kt = 0; kt < kKT; ++kt) S2[a][u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < QT; ++u) {
-      floatx4 S[kKT];
+      for (int s = 0; s < kS; ++s) {
+        bf16x8_t kf[kKT];
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
-      // the chunk max, taken from the reference m on (the growth test below
-      // compares with m anyway); NaN-propagating maxima need no quieting of
-      // their inputs, which saves an instruction per operand the compiler
-      // cannot prove canonical
-      float mc = m[u];
+        for (int kt = 0; kt < kKT; ++kt)
+          kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+        for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mc = __builtin_elementwise_maximum(mc, S[kt][i]);
-      // the reference max of a row moves only when the chunk's max exceeds it
-      // by more than kLazy in the exponent (always on the first chunk, where
-      // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
-      // does not depend on the reference
-      mc = __builtin_elementwise_maximum(
-          mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc), 0x401F)));
-      const float mc_w = __builtin_elementwise_maximum(
-          mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc))));
-      const bool grow = (mc_w - m[u]) * c2 > kLazy;
-      const float m_new = grow ? mc_w : m[u];
-      const float nm = -m_new * c2;
-      floatx4 P[kKT];
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
-      if (__any(grow)) {  // wave-uniform
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
-        Ls[u][0] *= alpha;
-#pragma unroll
-        for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+          for (int u = 0; u < QT; ++u) {
+            ST_BEFORE(kf[kt]);
+            S2[s % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[u][s], S2[s % kAcc][u][kt], 0, 0, 0);
+            ST_AFTER(S2[s % kAcc][u][kt]);
+            ST_PIN_MFMA();
+          }
       }
-      m[u] = m_new;
+      // mask k-step: the window has a cut or padding, or this chunk runs past N
+      if (cur.masked || (c + 1) * kKC > p.g.N) {
+        bf16x8_t xf[kKT];
 #pragma unroll
-      for (int j = 0; j < kJ; ++j)
-        Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
-                                           __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
-      Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
-    }
-
-    // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
-    // once for the wave's QT query tiles ----
+        for (int kt = 0; kt < kKT; ++kt)
+          xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      u32x4 vf[kT];
+        for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        const int d = dbase(t, qd);
-        const int lo_off = v_off<DH>(32 * j + 4 * g4 + e, d);
-        const int hi_off = v_off<DH>(32 * j + 16 + 4 * g4 + e, d);
-        const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
-        const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
-        vf[t] = u32x4{a[0], a[1], b[0], b[1]};
+          for (int u = 0; u < QT; ++u) {
+            ST_BEFORE(xf[kt]);
+            S2[kS % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb[u], S2[kS % kAcc][u][kt], 0, 0, 0);
+            ST_AFTER(S2[kS % kAcc][u][kt]);
+            ST_PIN_MFMA();
+          }
       }
-#pragma unroll
-      for (int t = 0; t < kT; ++t)
-#pragma unroll
-        for (int u = 0; u < QT; ++u) {
-          O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
-          ST_PIN_MFMA();
-        }
+
+      // ---- online softmax, per query tile ----
+      bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
+      bf16x4_t Pt[QT];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        ST_BEFORE(ones8);
-        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[u][j], Ls[u], 0, 0, 0);
-        ST_AFTER(Ls[u]);
-        ST_PIN_MFMA();
+        floatx4 S[kKT];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
+        // the chunk max, taken from the reference m on (the growth test below
+        // compares with m anyway); NaN-propagating maxima need no quieting of
+        // their inputs, which saves an instruction per operand the compiler
+        // cannot prove canonical
+        float mc = m[u];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mc = __builtin_elementwise_maximum(mc, S[kt][i]);
+        // the reference max of a row moves only when the chunk's max exceeds it
+        // by more than kLazy in the exponent (always on the first chunk, where
+        // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
+        // does not depend on the reference
+        mc = __builtin_elementwise_maximum(
+            mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc), 0x401F)));
+        const float mc_w = __builtin_elementwise_maximum(
+            mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc))));
+        const bool grow = (mc_w - m[u]) * c2 > kLazy;
+        const float m_new = grow ? mc_w : m[u];
+        const float nm = -m_new * c2;
+        floatx4 P[kKT];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
+        if (__any(grow)) {  // wave-uniform
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
+          Ls[u][0] *= alpha;
+#pragma unroll
+          for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+        }
+        m[u] = m_new;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
+                                             __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
+        Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
       }
-    }
-    if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
-      short4_t vt[kT];
+
+      // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
+      // once for the wave's QT query tiles ----
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        const int d = dbase(t, qd);
-        const int key = 32 * kJ + 4 * g4 + e;
-        vt[t] = lds_tr(vb, v_off<DH>(key, d));
-      }
+      for (int j = 0; j < kJ; ++j) {
+        u32x4 vf[kT];
 #pragma unroll
-      for (int t = 0; t < kT; ++t)
-#pragma unroll
-        for (int u = 0; u < QT; ++u) {
-          O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
-          ST_PIN_MFMA();
+        for (int t = 0; t < kT; ++t) {
+          const int d = dbase(t, qd);
+          const int lo_off = v_off<DH>(32 * j + 4 * g4 + e, d);
+          const int hi_off = v_off<DH>(32 * j + 16 + 4 * g4 + e, d);
+          const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
+          const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
+          vf[t] = u32x4{a[0], a[1], b[0], b[1]};
         }
 #pragma unroll
-      for (int u = 0; u < QT; ++u) {
-        ST_BEFORE(ones4);
-        Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
-        ST_AFTER(Ls[u]);
-        ST_PIN_MFMA();
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int u = 0; u < QT; ++u) {
+            O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
+            ST_PIN_MFMA();
+          }
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          ST_BEFORE(ones8);
+          Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[u][j], Ls[u], 0, 0, 0);
+          ST_AFTER(Ls[u]);
+          ST_PIN_MFMA();
+        }
+      }
+      if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
+        short4_t vt[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          const int d = dbase(t, qd);
+          const int key = 32 * kJ + 4 * g4 + e;
+          vt[t] = lds_tr(vb, v_off<DH>(key, d));
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int u = 0; u < QT; ++u) {
+            O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
+            ST_PIN_MFMA();
+          }
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          ST_BEFORE(ones4);
+          Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
+          ST_AFTER(Ls[u]);
+          ST_PIN_MFMA();
+        }
       }
     }
 
@@ -546,19 +565,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const uint16_t* kcol = k + hoff + 8 * my_ch;
   const uint16_t* vcol = v + hoff + 8 * my_ch;
   uint32_t padk = 0;  // bit j: load j of this thread is a padding slot's stand-in
+  // The kCh lanes that load one row share its slot map: lane (chunk) c maps
+  // the rows of loads c, c + kCh, ... (and, in windows with a cut or padding,
+  // writes their region codes for the mask step); every lane takes the token
+  // of its load j from lane j mod kCh of its group by a permute, bit 31
+  // flagging a padding slot.
+  static_assert(kCh == 8 || kCh == 16, "row groups inside one wave");
+  constexpr int kMap = (kPer + kCh - 1) / kCh;
+  const int gbase = (lane & ~(kCh - 1)) * 4;  // byte address of the group's first lane
   auto gather = [&](auto edge) {
     constexpr bool kEdge = decltype(edge)::value;
+    int32_t mtok[kMap];
+#pragma unroll
+    for (int m = 0; m < kMap; ++m) {
+      const int j = my_ch + kCh * m;
+      const int r = my_row + (kThreads / kCh) * j;
+      mtok[m] = 0;
+      if (j < kPer && r < kN) {
+        if (kEdge) {
+          int32_t t;
+          uint32_t code;
+          map_slot(p.g, cur, (uint32_t)r, t, code);
+          codeS[r] = (uint8_t)code;
+          mtok[m] = code == kPadSlot ? (int32_t)((uint32_t)t | 0x80000000u) : t;
+        } else {
+          mtok[m] = map_slot_plain(p.g, cur, (uint32_t)r);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int r = my_row + (kThreads / kCh) * j;
       if (r < kN) {
-        int32_t t;
+        int32_t t = __builtin_amdgcn_ds_bpermute(gbase + 4 * (j % kCh), mtok[j / kCh]);
         if (kEdge) {
-          uint32_t code;
-          map_slot(p.g, cur, (uint32_t)r, t, code);
-          padk |= code == kPadSlot ? 1u << j : 0u;
-        } else {
-          t = map_slot_plain(p.g, cur, (uint32_t)r);
+          padk |= t < 0 ? 1u << j : 0u;
+          t &= 0x7FFFFFFF;
         }
         kr[j] = ldg16(kcol + row_at(t, p.sk));
         vr[j] = ldg16(vcol + row_at(t, p.sv));
@@ -600,14 +642,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       *reinterpret_cast<u32x4*>(smem + L::kTensor + row_off<DH>(r, my_ch)) = vr[j];
     }
   }
-  // region codes and mask-feature tables: windows with a cut or padding only
+  // mask-feature tables: windows with a cut or padding only (their region
+  // codes were written during the gather)
   if (cur.masked) {
-    for (int r = tid; r < kN; r += kThreads) {
-      int32_t t;
-      uint32_t c;
-      map_slot(p.g, cur, (uint32_t)r, t, c);
-      codeS[r] = (uint8_t)c;
-    }
     if (tid < 72) {
       const int e = tid;
       const uint32_t ck = (e < 36 ? e : e - 36) >> 2, part = e & 3;
