@@ -48,15 +48,22 @@ def log(msg):
 
 
 def algorithmic_work(wl):
-    """Bytes: read Q, K, V and write O once per real token. FLOPs: 4 N^2 dh per window-head."""
+    """Bytes: read Q, K, V and write O once per real token. FLOPs: 4 n^2 dh per window-head, n the
+    real (not padding) slots of the window: the dense products among its real tokens, masked or
+    not (N^2 where the grid needs no padding). The real slots of a window are the product over the
+    axes of its real positions along each, so the sum of n^2 over windows is the product over the
+    axes of the sums of squares."""
     elt = 2 if wl.dtype == "bf16" else 4
     nbytes = 4 * wl.tokens * wl.heads * wl.head_dim * elt
     n = 1
-    for x, w in zip((wl.D, wl.H, wl.W), wl.window):
-        n *= -(-x // w)
+    sq = 1
+    for x, w, s in zip((wl.D, wl.H, wl.W), wl.window, wl.shift):
+        nw = -(-x // w)
+        P = nw * w
+        n *= nw
+        sq *= sum(sum(1 for o in range(w) if (k * w + o + s) % P < x) ** 2 for k in range(nw))
     n *= wl.B
-    N = wl.window[0] * wl.window[1] * wl.window[2]
-    flops = 4 * N * N * wl.head_dim * wl.heads * n
+    flops = 4 * sq * wl.B * wl.head_dim * wl.heads
     return nbytes, flops, n
 
 

@@ -117,7 +117,7 @@ __device__ __forceinline__ int v_off(int key, int d) {
 }
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
-template <int DH, int WAVES, int KC, int QT>
+template <int DH, int WAVES, int KC, int QT, bool kPad>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
@@ -171,8 +171,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
   }
   // a block whose query slots are all padding writes nothing: it ends here
-  // (in windows that hold padding only: a wave-uniform test)
-  if (cur.padded || (qb + 1) * kQB > p.g.N) {
+  // (kPad: the grid needs padding; only windows that hold padding can have
+  // such blocks, a wave-uniform test)
+  if (kPad && cur.padded) {
     if (!__syncthreads_or(any_real)) return;
   }
 
@@ -190,10 +191,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   const int my_row = tid / kCh, my_ch = tid % kCh;
   const uint16_t* kcol = k + hoff + 8 * my_ch;
   const uint16_t* vcol = v + hoff + 8 * my_ch;
-  // Padding slots (and slots past N) load a stand-in token; their K and V rows
-  // are replaced by zeros before they reach LDS, so the stand-in's values never
-  // reach an output (an Inf or NaN in it stays in its own window). Ring entries
-  // carry that flag in bit 31 (tokens are below 2^31).
+  // Padding slots (and slots past N) load a stand-in, token 0; their K and V
+  // rows are replaced by zeros before they reach LDS, so the stand-in's values
+  // never reach an output (an Inf or NaN in it stays in its own window). Ring
+  // entries carry that flag in bit 31 (tokens are below 2^31).
   uint32_t padk = 0;  // bit i: load i of the chunk in flight is a padding slot's stand-in
   auto fetch = [&](int c) {
     padk = 0;
@@ -201,15 +202,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     for (int i = 0; i < kLoads; ++i) {
       const int r = my_row + (kThreads / kCh) * i;
       int32_t t;
+      bool pad;
       if (c == 0) {
         uint32_t code;
         map_slot(p.g, cur, (uint32_t)r, t, code);
-        padk |= code == kPadSlot ? 1u << i : 0u;
+        pad = code == kPadSlot;
       } else {
         t = tok_ring[(c % kRing) * kKC + r];
-        padk |= t < 0 ? 1u << i : 0u;
-        t &= 0x7FFFFFFF;
+        pad = t < 0;
       }
+      padk |= pad ? 1u << i : 0u;
+      // every padding slot of the chunk reads token 0 instead of its own
+      // stand-in: the same few lines, served from the caches
+      t = pad ? 0 : t;
       // ordinary (not non-temporal) loads: the query blocks of a window read
       // the same K and V rows one after another on one XCD, from its L2
       kr[i] = *reinterpret_cast<const u32x4*>(kcol + row_at(t, p.sk));
@@ -309,11 +314,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     // c - 1) finished before the previous barrier
     if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
 
-    // ---- a chunk of padding keys only (in a window that holds padding, or
-    // past N) adds nothing: their weights are exactly zero, so it is skipped
+    // ---- a chunk of padding keys only (possible in a window that holds
+    // padding) adds nothing: their weights are exactly zero, so it is skipped
     // (wave-uniform: every wave reads the same codes) ----
     bool skip = false;
-    if (cur.padded || (c + 1) * kKC > p.g.N) {
+    if (kPad && cur.padded) {
       bool kp = true;
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) kp = kp && cb[kt * 16 + l16] == kPadSlot;
@@ -843,8 +848,12 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   uint16_t* oo = static_cast<uint16_t*>(o);
   void* args[] = {&qq, &kk, &vv, &oo, &p};
   const dim3 grid((unsigned)((pl->n_windows + 7) / 8 * 8 * p.nqb), (unsigned)pl->desc.heads);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT>), grid,
-                         dim3(64 * WAVES), args, 0, s);
+  // grids that need padding get the instance that skips query blocks and key
+  // chunks of padding only
+  const bool pad = pl->padded[0] != pl->desc.D || pl->padded[1] != pl->desc.H || pl->padded[2] != pl->desc.W;
+  return hipLaunchKernel(pad ? reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, true>)
+                             : reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, false>),
+                         grid, dim3(64 * WAVES), args, 0, s);
 }
 
 template <int DH, int NT>

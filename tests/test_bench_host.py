@@ -22,12 +22,41 @@ def test_algorithmic_work_stage1():
     assert flops == 4 * 144 * 144 * 64 * 8 * 1800 == 76_441_190_400
 
 
+def _real_slot_squares(wl):
+    """Sum over windows of (real slots)^2, by visiting every slot of every window."""
+    P = [-(-x // w) * w for x, w in zip((wl.D, wl.H, wl.W), wl.window)]
+    total = 0
+    for kd in range(P[0] // wl.window[0]):
+        for kh in range(P[1] // wl.window[1]):
+            for kw in range(P[2] // wl.window[2]):
+                n = 0
+                for od in range(wl.window[0]):
+                    for oh in range(wl.window[1]):
+                        for ow in range(wl.window[2]):
+                            g = [(k * w + o + s) % p for k, w, o, s, p in
+                                 zip((kd, kh, kw), wl.window, (od, oh, ow), wl.shift, P)]
+                            n += g[0] < wl.D and g[1] < wl.H and g[2] < wl.W
+                total += n * n
+    return total * wl.B
+
+
 def test_algorithmic_work_counts_real_tokens_only():
-    """Stage 3 pads 45 x 90 to 48 x 96: bytes count the real tokens, FLOPs every padded window."""
-    nbytes, flops, nwin = bench.algorithmic_work(datagen.WORKLOADS["stage3_pad"])
+    """Stage 3 pads 45 x 90 to 48 x 96: bytes count the real tokens, FLOPs the products among the
+    real tokens of each window (the last window along H holds 3 real rows of 6, along W 6 real
+    columns of 12)."""
+    wl = datagen.WORKLOADS["stage3_pad"]
+    nbytes, flops, nwin = bench.algorithmic_work(wl)
     assert nbytes == 4 * (4 * 45 * 90) * 32 * 64 * 2
     assert nwin == 2 * 8 * 8
-    assert flops == 4 * 144 * 144 * 64 * 32 * 128
+    assert _real_slot_squares(wl) == (2 * 2 ** 2) * (7 * 6 ** 2 + 3 ** 2) * (7 * 12 ** 2 + 6 ** 2)
+    assert flops == 4 * _real_slot_squares(wl) * 64 * 32
+    assert flops < 4 * 144 * 144 * 64 * 32 * 128
+
+
+@pytest.mark.parametrize("name", ["stage1_w3x12x12_h4d128", "stage1_w4x12x24", "tiny_f32"])
+def test_algorithmic_flops_brute_force(name):
+    wl = datagen.WORKLOADS[name]
+    assert bench.algorithmic_work(wl)[1] == 4 * _real_slot_squares(wl) * wl.head_dim * wl.heads
 
 
 def test_traffic_summary_matches_the_kernel_source():
