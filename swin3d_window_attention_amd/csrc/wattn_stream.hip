@@ -371,31 +371,41 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
           }
       }
 
-      // ---- online softmax, per query tile ----
+      // ---- online softmax. The chunk maxima of all QT tiles first, then their
+      // lane exchanges side by side (each waits on the LDS crossbar once for
+      // all tiles), then the exponentials ----
       bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
       bf16x4_t Pt[QT];
+      floatx4 S[QT][kKT];
+      float mc[QT];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        floatx4 S[kKT];
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) S[kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
+        for (int kt = 0; kt < kKT; ++kt) S[u][kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
         // the chunk max, taken from the reference m on (the growth test below
         // compares with m anyway); NaN-propagating maxima need no quieting of
         // their inputs, which saves an instruction per operand the compiler
         // cannot prove canonical
-        float mc = m[u];
+        mc[u] = m[u];
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mc = __builtin_elementwise_maximum(mc, S[kt][i]);
+          for (int i = 0; i < 4; ++i) mc[u] = __builtin_elementwise_maximum(mc[u], S[u][kt][i]);
+      }
+      int xs[QT];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc[u]), 0x401F);
+#pragma unroll
+      for (int u = 0; u < QT; ++u) mc[u] = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
+#pragma unroll
+      for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc[u]));
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        const float mc_w = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
         // the reference max of a row moves only when the chunk's max exceeds it
         // by more than kLazy in the exponent (always on the first chunk, where
         // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
         // does not depend on the reference
-        mc = __builtin_elementwise_maximum(
-            mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc), 0x401F)));
-        const float mc_w = __builtin_elementwise_maximum(
-            mc, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc))));
         const bool grow = (mc_w - m[u]) * c2 > kLazy;
         const float m_new = grow ? mc_w : m[u];
         const float nm = -m_new * c2;
@@ -403,7 +413,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[kt][i], c2, nm));
+          for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[u][kt][i], c2, nm));
         if (__any(grow)) {  // wave-uniform
           const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
           Ls[u][0] *= alpha;

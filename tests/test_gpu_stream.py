@@ -32,6 +32,12 @@ SMALL = [
     wl_of("w16x16x16_max", 1, 16, 16, 20, 1, 64, (16, 16, 16), (8, 4, 10)),  # N = 4096, the largest window
     wl_of("dh32", 1, 4, 13, 25, 3, 32, (2, 6, 12), (1, 3, 6)),           # head_dim 32, N = 144
     wl_of("dh32_w2x6x6", 2, 3, 10, 14, 2, 32, (2, 6, 6), (1, 3, 3)),      # head_dim 32, N = 72
+    # D padded 4 -> 6: in the second D-window two of three depth planes are padding, so whole
+    # query blocks and whole 48-key chunks hold padding only (the skipping instance)
+    wl_of("w3x12x12_d4pad", 1, 4, 24, 24, 2, 128, (3, 12, 12), (1, 6, 6)),
+    # D padded 3 -> 4: the second D-window's first depth plane (64 slots) is padding, one whole
+    # 64-key chunk of the four
+    wl_of("w2x8x8_d3pad", 1, 3, 16, 24, 3, 64, (2, 8, 8), (1, 4, 4)),
 ]
 
 
