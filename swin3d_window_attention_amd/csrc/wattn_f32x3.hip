@@ -111,25 +111,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const WinPos cur = decode_window(p.g, blockIdx.x);
   const size_t hoff = (size_t)head * 64;
 
-  // ---- gather: K and V rows whole (sixteen lanes x 16 B per 256-byte row),
-  // each thread mapping the slots it loads ----
+  // ---- gather: K and V rows whole (sixteen lanes x 16 B per 256-byte row).
+  // The sixteen lanes of a row share its slot map: the lane of chunk j maps
+  // the row of the group's load j and writes that row's slot table entry
+  // (token, region code) for the mask and the scatter; every lane takes the
+  // token of its load j from that lane by a permute, bit 31 flagging a
+  // padding slot ----
   constexpr int kChunks = kN * 16;
   constexpr int kPer = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+  static_assert(kChunks % kThreads == 0 && kPer <= 16, "whole chunks per thread, one row per lane");
   // Padding slots load a stand-in token; their K and V rows are replaced by
   // zeros before they reach LDS, so the stand-in's values never reach an
   // output (an Inf or NaN in it stays in its own window).
   u32x4 kr[kPer], vr[kPer];
   uint32_t padk = 0;  // bit j: load j is a padding slot's stand-in
+  const int gbase = (lane & ~15) * 4;  // byte address of the row group's first lane
+  int32_t mtok = 0;
+  if ((tid & 15) < kPer) {
+    const int r = (tid >> 4) + (kThreads / 16) * (tid & 15);
+    int32_t t;
+    uint32_t code;
+    map_slot<false>(p.g, cur, (uint32_t)r, t, code);
+    tokS[r] = t;
+    codeS[r] = (uint8_t)code;
+    mtok = code == kPadSlot ? (int32_t)((uint32_t)t | 0x80000000u) : t;
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int c = tid + kThreads * j;
-    int32_t t;
-    uint32_t code;
-    map_slot<false>(p.g, cur, (uint32_t)(c >> 4), t, code);
+    int32_t t = __builtin_amdgcn_ds_bpermute(gbase + 4 * j, mtok);
+    padk |= t < 0 ? 1u << j : 0u;
+    t &= 0x7FFFFFFF;
     kr[j] = ldg16(k + (size_t)t * p.sk + hoff + 4 * (c & 15));
     vr[j] = ldg16(v + (size_t)t * p.sv + hoff + 4 * (c & 15));
-    padk |= code == kPadSlot ? 1u << j : 0u;
   }
   // Q straight into the operand layout: lane (g4, query l16) of a tile holds
   // dims [8 g4, 8 g4 + 8) and the same + 32 of its query row
@@ -168,16 +182,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     *reinterpret_cast<u32x2*>(smem + kVh + off) = h;
     *reinterpret_cast<u32x2*>(smem + kVl + off) = l;
   }
-  // ---- slot table (token, region code) for the mask and the scatter ----
-  for (int r = tid; r < kN; r += kThreads) {
-    int32_t t;
-    uint32_t c;
-    map_slot<false>(p.g, cur, (uint32_t)r, t, c);
-    tokS[r] = t;
-    codeS[r] = (uint8_t)c;
-  }
   // ---- mask-feature tables (windows with a cut or padding only), built by
-  // the wave that has no slots to map ----
+  // the last wave (the slot table was written during the gather) ----
   if (cur.masked && tid >= kThreads - 64) {
     for (int e = tid - (kThreads - 64); e < 72; e += 64) {
       const uint32_t ck = (e < 36 ? e : e - 36) >> 2, part = e & 3;
