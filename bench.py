@@ -32,6 +32,7 @@ KERNEL_SRC = os.path.join(ROOT, "swin3d_window_attention_amd", "csrc", "wattn_bf
 # every input of the headline launch: the kernel, the host code that builds its
 # plan and arguments, the public header, and the build script (compiler flags)
 LAUNCH_INPUTS = [KERNEL_SRC] + [os.path.join(ROOT, *f) for f in (
+    ("swin3d_window_attention_amd", "csrc", "fastdiv.h"),
     ("swin3d_window_attention_amd", "csrc", "plan.h"),
     ("swin3d_window_attention_amd", "csrc", "api.cpp"),
     ("include", "swin3d_wattn.h"),

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
 #include "plan.h"
 
 namespace {
@@ -28,21 +29,9 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 constexpr int kWaves = 4;
 constexpr int kMaxUnits = 16;  // C <= 64 lanes x 16 units x 4 channels = 4096
 
-struct FastDiv {
-  uint32_t mul, shr;
-};
-
-// floor(n / d) for 0 <= n < 2^31 (Granlund and Montgomery, PLDI 1994, Theorem 4.2)
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint32_t shr = 31 + l;
-  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
-}
+using fastdiv::FastDiv;
+using fastdiv::fdiv;
+using fastdiv::make_fastdiv;
 
 struct AdalnParams {
   int32_t rows;   // B * T

@@ -15,6 +15,7 @@
 
 #include <type_traits>
 
+#include "fastdiv.h"
 #include "plan.h"
 
 namespace {
@@ -85,27 +86,12 @@ constexpr int kCodeOff = kQtOff + 9 * 4 * 16;
 constexpr int kTokOff = kCodeOff + kN;
 constexpr int kSmemBytes = kTokOff + kN * 4;
 
-// floor(n / d) for 0 <= n < 2^31 as (n * mul) >> shr: with l = ceil(log2 d),
-// shr = 31 + l and mul = ceil(2^shr / d), the product error stays below one
-// step of n (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", PLDI 1994, Theorem 4.2 with N = 31)
-struct FastDiv {
-  uint32_t mul, shr;
-};
+using fastdiv::FastDiv;
+using fastdiv::fdiv;
+using fastdiv::make_fastdiv;
 
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint32_t shr = 31 + l;
-  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
-}
-
-// The same for the per-lane slot arithmetic, where n < 2^8 (a slot of the
-// 144-token window) and d <= 2^12, with a fixed shift in full-rate 24-bit
+// Division as in fastdiv.h, for the per-lane slot arithmetic, where n < 2^8
+// (a slot of the 144-token window) and d <= 2^12, with a fixed shift in full-rate 24-bit
 // operations: mul = ceil(2^20 / d) <= 2^20, so n * mul < 2^28, and the error
 // term n * (mul * d - 2^20) < 2^8 * 2^12 stays below 2^20: the quotient is
 // exact, and it is known to fit 12 bits, so it feeds the next 24-bit product

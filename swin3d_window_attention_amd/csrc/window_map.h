@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
 #include "plan.h"
 
 namespace wmap {
@@ -21,23 +22,9 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 
 constexpr uint32_t kPadSlot = 8;  // region code of a padding slot
 
-// floor(n / d) for 0 <= n < 2^31 as (n * mul) >> shr with shr = 31 + ceil(log2 d)
-// and mul = ceil(2^shr / d) (Granlund and Montgomery, "Division by invariant
-// integers using multiplication", PLDI 1994, Theorem 4.2 with N = 31)
-struct FastDiv {
-  uint32_t mul, shr;
-};
-
-inline FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint32_t shr = 31 + l;
-  return FastDiv{(uint32_t)(((uint64_t(1) << shr) + d - 1) / d), shr};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (uint32_t)(((uint64_t)n * f.mul) >> f.shr);
-}
+using fastdiv::FastDiv;
+using fastdiv::fdiv;
+using fastdiv::make_fastdiv;
 
 // Grid, padding, shift and window of a plan, and the windows that hold a
 // region cut or padding along each axis (-1 = none)
