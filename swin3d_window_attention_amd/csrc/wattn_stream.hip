@@ -331,6 +331,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       // accumulate separately, so that no MFMA takes its accumulator from one
       // of the three before it ----
       constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
+      // the wave's priority is raised while it issues matrix-core work, so
+      // that of the waves of a SIMD the one with products ready goes first
+      // and the others' vector work fills in behind it
+      __builtin_amdgcn_s_setprio(1);
       floatx4 S2[kAcc][QT][kKT];
 #pragma unroll
       for (int a = 0; a < kAcc; ++a)
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
           }
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // ---- online softmax. The chunk maxima of all QT tiles first, then their
       // lane exchanges side by side (each waits on the LDS crossbar once for
       // all tiles), then the exponentials ----
@@ -428,6 +433,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
         Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
       }
 
+      __builtin_amdgcn_s_setprio(1);
       // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
       // once for the wave's QT query tiles ----
 #pragma unroll
@@ -480,6 +486,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
           ST_PIN_MFMA();
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // ---- next chunk into the other buffer (everyone finished chunk c - 1,
