@@ -31,11 +31,13 @@
  * before P V and O is rounded to bf16 (nearest-even) at the end. f32 I/O
  * computes everything in FP32 (FP32 matrix-core products, FP32 softmax);
  * f32 I/O with F32_SPLIT runs the products as three bf16 matrix-core
- * products each. The kernels load the nearest real token into each padding
+ * products each. The kernels load a real stand-in token for each padding
  * slot of a window (so every load is unconditional) and replace its K and V
  * rows by zeros before use, so padding adds exactly nothing: an Inf or NaN in
  * a real token affects only the outputs of its own window, as in a
- * materialised pad-shift-partition pipeline.
+ * materialised pad-shift-partition pipeline. On grids that need padding the
+ * K/V-streaming kernel skips the query blocks and key chunks that hold
+ * padding only (their outputs are cropped, their weights exactly zero).
  *
  * Ownership: the caller owns every device buffer. The library allocates no
  * device memory; a plan is a small immutable host object.
