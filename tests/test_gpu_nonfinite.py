@@ -1,7 +1,8 @@
 """Padding slots are immune to what their stand-in token holds.
 
-Every kernel fills a window's padding slots by loading the nearest real token
-(its coordinates clamped to the grid), so that all loads are unconditional.
+Every kernel fills a window's padding slots by loading a real stand-in token,
+so that all loads are unconditional: the nearest real token (its coordinates
+clamped to the grid), or token 0 in the K/V-streaming kernel.
 The padding exclusion of the pages' scope (padded key positions masked out,
 padded query rows cropped) must then hold for any input: here an Inf or NaN
 is planted in Q, K and V of a real token that serves as such a stand-in for
@@ -107,3 +108,43 @@ def test_nonfinite_stand_in_stays_in_its_window(case, bias):
         gn, vn, _ = oracle.window_slot_coords(grid, window, shift, (kd, kh, kw))
         assert keep[tuple(gn[vn].T)].all()
     check(wl, got[0][keep], ref[0][keep], f"outside the planted window, bias={bias}")
+
+
+@pytest.mark.parametrize("bias", [-100.0, -math.inf], ids=["bias-100", "bias-inf"])
+def test_stream_token0_stand_in(bias):
+    """The K/V-streaming kernel loads token 0 for every padding slot (the same lines for all, from
+    the caches): with Inf / NaN planted in token 0, every window that holds padding loads it, and
+    all of them must still match the oracle."""
+    grid, window, shift = (3, 10, 12), (2, 6, 8), (1, 3, 4)  # N = 96, padded to 4 x 12 x 16
+    wl = datagen.small_workload("nonfinite_stream_token0", 1, *grid, 2, 64, window, shift, "bf16", seed=84)
+    host = {t: datagen.full_io(wl, t) for t in "qkv"}
+    _plant(host, "bf16", (0, 0, 0, 0))
+    x = {t: datagen.to_torch(host[t], "bf16").to("cuda") for t in "qkv"}
+    plan = sw.Plan(*wl.shape, window=window, shift=shift, dtype="bf16", scale=wl.scale, cross_region_bias=bias)
+    assert plan.info().kernel == 3
+    o = torch.full_like(x["q"], float("nan"))
+    say(f"[gpu] run {wl.name} shape={wl.shape} window={window} shift={shift} bias={bias}")
+    plan.run(x["q"], x["k"], x["v"], o)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy().astype(np.float64)
+    widen = lambda a: datagen.bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.swin3d_window_attention(widen(host["q"]), widen(host["k"]), widen(host["v"]), window, shift,
+                                             wl.scale, bias)
+    P = [oracle.padded_extent(x_, w) for x_, w in zip(grid, window)]
+    own = tuple(((0 - s) % p) // w for s, p, w in zip(shift, P, window))
+    g, valid, _ = oracle.window_slot_coords(grid, window, shift, own)
+    own_mask = np.zeros(grid, dtype=bool)
+    own_mask[tuple(g[valid].T)] = True
+    bad_ref = ~np.all(np.isfinite(ref[0]), axis=(-2, -1))
+    assert bad_ref.any() and not np.any(bad_ref & ~own_mask), "oracle leaked outside the planted window"
+    # windows other than the planted one that hold padding (and so load token 0 as a stand-in)
+    padded_others = 0
+    nwin = [p // w for p, w in zip(P, window)]
+    for kd in range(nwin[0]):
+        for kh in range(nwin[1]):
+            for kw in range(nwin[2]):
+                _, vn, _ = oracle.window_slot_coords(grid, window, shift, (kd, kh, kw))
+                padded_others += (kd, kh, kw) != own and not vn.all()
+    assert padded_others > 0
+    check(wl, got[0][~own_mask], ref[0][~own_mask], f"outside the planted window, bias={bias}")
