@@ -3,8 +3,10 @@
 //
 // This is the FP32 path of the method at matrix-core speed: both products
 // run on v_mfma_f32_16x16x4_f32 (FP32 operands, FP32 accumulation, no
-// reduced-precision step anywhere), and the shifted-window mask, the
-// softmax and P stay in FP32 on the vector ALU. The Flash-Aurora README
+// reduced-precision step anywhere); the shifted-window mask is the FP32
+// initial value of the Q K^T accumulators, read from a per-window table of
+// query code x key terms, and the softmax and P stay in FP32 on the vector
+// ALU. The Flash-Aurora README
 // ("Window attention kernels", "CuTe DSL window attention") keeps the whole
 // window's K and V in one shared-memory tile; so does this kernel.
 //
@@ -63,7 +65,8 @@ struct Lds {
   static constexpr int kVt = kN * DH * 4;            // V^T, DH x kVtPitch floats
   static constexpr int kCode = kVt + DH * kVtPitch * 4;
   static constexpr int kTok = kCode + kN;            // 4-byte aligned: kN is a multiple of 16
-  static constexpr int kBytes = kTok + kN * 4;
+  static constexpr int kBias = kTok + kN * 4;        // mask terms, 9 query codes x kN keys floats
+  static constexpr int kBytes = kBias + 9 * kN * 4;
 };
 
 struct AttnParams {
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   uint8_t* codeS = smem + L::kCode;
   int32_t* tokS = reinterpret_cast<int32_t*>(smem + L::kTok);
   float* vt = reinterpret_cast<float*>(smem + L::kVt);
+  float* biasS = reinterpret_cast<float*>(smem + L::kBias);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,8 +111,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   const int x32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   const int head = blockIdx.y;
   const WinPos cur = decode_window(p.g, blockIdx.x);
-  // kTail: the last tile holds slots past N (padding), so the mask step always runs
-  const bool masked = cur.masked || kTail;
   const size_t hoff = (size_t)head * DH;
   // query tiles of this wave: (wave - rot) mod 4 + 4 i; the rotation moves
   // the three-tile share from wave to wave across workgroups
@@ -122,8 +124,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   // output (an Inf or NaN in it stays in its own window).
   // The kCh lanes that load one row share its slot map: lane (chunk) ch maps
   // the row of load ch and writes the slot table entry (token, region code)
-  // of that row; every lane takes the token of its load j from lane j of its
-  // group by a permute, bit 31 flagging a padding slot.
+  // of that row and that key's column of the mask table (the term added to
+  // Q K^T for each of the nine query codes); every lane takes the token of
+  // its load j from lane j of its group by a permute, bit 31 flagging a
+  // padding slot.
   static_assert((kCh == 8 || kCh == 16) && kPer <= kCh, "row groups inside one wave, one row per lane");
   u32x4 kr[kPer], vr[kPer];
   uint32_t padk = 0;  // bit j: load j is a padding slot's stand-in
@@ -138,6 +142,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
       tokS[r] = t;
       codeS[r] = (uint8_t)code;
       mtok = code == kPadSlot ? (int32_t)((uint32_t)t | 0x80000000u) : t;
+      // mask term of key r for a query of code c, in the units of Q K^T: the
+      // cross-region bias / scale where both are real and their regions
+      // differ, -inf for a padding key, 0 otherwise (a padding query, never
+      // written, takes no bias; in a window without a cut or padding every
+      // slot has code 0, so the row its queries read is all zeros)
+#pragma unroll
+      for (uint32_t c = 0; c <= kPadSlot; ++c)
+        biasS[c * kN + r] = code == kPadSlot ? -INFINITY : (c != kPadSlot && code != c ? p.bias_s : 0.f);
     }
   }
 #pragma unroll
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
   // (the slot table for the mask and the scatter was written during the gather)
   __syncthreads();
 
-  const float c2 = p.c2, bias_s = p.bias_s;
+  const float c2 = p.c2;
   floatx4 qn[kQC];  // beyond ten tiles: the next tile's Q, loaded during this one
 #pragma unroll
   for (int qi = 0; qi < kMaxQT; ++qi) {
@@ -205,11 +217,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
 
     // ---- S^T = K Q^T: k-step s = 4 c + e of lane group kk is dim kk DH/4 + s ----
     // with fewer than four key tiles, k-step s accumulates into set s % kAccS,
-    // so that no MFMA takes its accumulator from one of the three before it
+    // so that no MFMA takes its accumulator from one of the three before it.
+    // The first set starts from the mask terms of this lane's query code and
+    // keys (the cross-region bias / scale where the two regions differ, -inf
+    // for a padding key, else 0), so the products accumulate onto the bias in
+    // the units of Q K^T.
+    const uint32_t qc = codeS[qt * 16 + l16];
     constexpr int kAccS = kNT >= 4 ? 1 : kNT == 1 ? 4 : 2;
     floatx4 S2[kAccS][kNT];
+    {
+      const float* brow = biasS + qc * kN + 4 * g4;
 #pragma unroll
-    for (int a = 0; a < kAccS; ++a)
+      for (int kt = 0; kt < kNT; ++kt) S2[0][kt] = *reinterpret_cast<const floatx4*>(brow + 16 * kt);
+    }
+#pragma unroll
+    for (int a = 1; a < kAccS; ++a)
 #pragma unroll
       for (int kt = 0; kt < kNT; ++kt) S2[a][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
     // beyond ten key tiles the K operands are read a group of tiles at a time
@@ -247,23 +269,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Lds<DH
       for (int a = 1; a < kAccS; ++a) S[kt] += S2[a][kt];
     }
 
-    // ---- shifted-window bias (bias / scale) and padding exclusion, added in
-    // the units of Q K^T; a padding query (never written) takes no bias. The
-    // row max is subtracted before scaling, so the largest weights see no
-    // rounding of a large scaled logit: p = 2^((s - max) scale log2(e)) ----
-    const uint32_t qc = codeS[qt * 16 + l16];
-    if (masked) {
-#pragma unroll
-      for (int kt = 0; kt < kNT; ++kt) {
-        const uint32_t kc4 = *reinterpret_cast<const uint32_t*>(codeS + kt * 16 + 4 * g4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t kc = (kc4 >> (8 * i)) & 0xFFu;
-          const float add = kc == kPadSlot ? -INFINITY : (qc != kPadSlot && kc != qc ? bias_s : 0.f);
-          S[kt][i] += add;
-        }
-      }
-    }
+    // ---- softmax: the row max is subtracted before scaling, so the largest
+    // weights see no rounding of a large scaled logit:
+    // p = 2^((s - max) scale log2(e)) ----
     float mx = S[0][0];
 #pragma unroll
     for (int kt = 0; kt < kNT; ++kt)

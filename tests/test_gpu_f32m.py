@@ -44,6 +44,8 @@ OTHER_WINDOWS = [
     # windows of 145 to 256 slots: 10 tiles, or 12, 14, 16 with the tail as padding
     datagen.small_workload("f32m_w2x8x10", 1, 4, 13, 25, 2, 64, (2, 8, 10), (1, 4, 5), "f32", 64),       # N = 160
     datagen.small_workload("f32m_w2x10x10", 1, 3, 17, 23, 2, 32, (2, 10, 10), (1, 5, 5), "f32", 65),     # N = 200
+    datagen.small_workload("f32m_w2x8x11", 1, 3, 17, 20, 2, 64, (2, 8, 11), (1, 4, 5), "f32", 69),       # N = 176
+    datagen.small_workload("f32m_w1x13x14_dh32", 1, 2, 15, 30, 2, 32, (1, 13, 14), (0, 6, 7), "f32", 70),  # N = 182
     datagen.small_workload("f32m_w2x7x15", 1, 4, 15, 29, 2, 64, (2, 7, 15), (1, 3, 7), "f32", 66),       # N = 210
     datagen.small_workload("f32m_w4x8x8", 1, 5, 17, 9, 2, 64, (4, 8, 8), (2, 4, 4), "f32", 67),          # N = 256
     datagen.small_workload("f32m_w4x8x8_dh32", 2, 4, 8, 16, 3, 32, (4, 8, 8), (0, 0, 0), "f32", 68),     # N = 256

@@ -52,6 +52,9 @@ def _kernels(asm_text):
 
 
 def stalled_mfma_war(instrs):
+    """(hits, MFMA count). An MFMA counts as stalled when a register of its SrcC still holds the
+    result of one of the previous NEAR_MFMAS MFMAs; a register that a load or a VALU op has
+    rewritten since (an accumulator started from a value in LDS, say) no longer does."""
     hits, mfmas, risky = [], [], []
     for i, line in enumerate(instrs):
         parts = re.split(r"[\s,]+", line)
@@ -60,7 +63,7 @@ def stalled_mfma_war(instrs):
         if op.startswith("v_mfma"):
             dst, a, b, c = (_regs(p) for p in parts[1:5])
             stalled = bool(c) and any(c & d for _, d in mfmas[-NEAR_MFMAS:])
-            mfmas.append((i, dst))
+            mfmas.append((i, set(dst)))
             if stalled:
                 risky.append((i, a | b, line))
             continue
@@ -69,6 +72,8 @@ def stalled_mfma_war(instrs):
             for j, srcs, text in risky:
                 if dst & srcs:
                     hits.append((j, i, text, line))
+            for _, d in mfmas[-NEAR_MFMAS:]:
+                d -= dst
     return hits, len(mfmas)
 
 
@@ -105,6 +110,18 @@ def test_scanner_flags_the_pattern():
           "v_mfma_f32_16x16x32_bf16 v[0:3], v[12:15], v[8:11], v[0:3]",
           "ds_read2_b64 v[12:15], v20 offset1:4"]
     assert stalled_mfma_war(ok)[0] == []
+    # an accumulator reloaded from LDS after the MFMA that last wrote it is not in flight
+    reloaded = ["v_mfma_f32_16x16x4_f32 v[0:3], v4, v8, v[0:3]",
+                "ds_read_b128 v[0:3], v20",
+                "v_mfma_f32_16x16x4_f32 v[0:3], v5, v8, v[0:3]",
+                "ds_read_b128 v[4:7], v20 offset:16"]
+    assert stalled_mfma_war(reloaded)[0] == []
+    # ... but a partial reload leaves the rest of the accumulator in flight
+    partial = ["v_mfma_f32_16x16x4_f32 v[0:3], v4, v8, v[0:3]",
+               "v_mov_b32_e32 v0, 0",
+               "v_mfma_f32_16x16x4_f32 v[0:3], v5, v8, v[0:3]",
+               "ds_read_b128 v[4:7], v20 offset:16"]
+    assert len(stalled_mfma_war(partial)[0]) == 1
 
 
 def test_no_stalled_mfma_operand_overwrite(asm):
