@@ -176,6 +176,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   if (kPad && cur.padded) {
     if (!__syncthreads_or(any_real)) return;
   }
+  // a wave whose query tiles hold padding or slots past N only (the last
+  // block of a window whose size is not a multiple of the block, or a block
+  // that runs into padding) still loads its share of every chunk and meets
+  // the barriers, but forms no scores and no products
+  const bool wave_real = __any(any_real);
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
   // (key row tid / kCh + i kThreads / kCh, chunk tid % kCh). Chunk 0 maps its own
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       for (int kt = 0; kt < kKT; ++kt) kp = kp && cb[kt * 16 + l16] == kPadSlot;
       skip = __all(kp);
     }
-    if (!skip) {
+    if (!skip && wave_real) {
       // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
       // for the wave's QT query tiles. Consecutive MFMAs take independent
       // accumulators: with fewer than four per k-step, even and odd k-steps
