@@ -166,21 +166,25 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     const int qslot = qb * kQB + (wave * QT + u) * 16 + l16;
     map_slot(p.g, cur, (uint32_t)qslot, qtok[u], qcode[u]);
     any_real |= qcode[u] != kPadSlot;
-#pragma unroll
-    for (int s = 0; s < kS; ++s)
-      qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
   }
-  // a block whose query slots are all padding writes nothing: it ends here
-  // (kPad: the grid needs padding; only windows that hold padding can have
-  // such blocks, a wave-uniform test)
+  // a block whose query slots are all padding writes nothing: it ends here,
+  // before loading anything (kPad: the grid needs padding; only windows that
+  // hold padding can have such blocks, a wave-uniform test)
   if (kPad && cur.padded) {
     if (!__syncthreads_or(any_real)) return;
   }
   // a wave whose query tiles hold padding or slots past N only (the last
   // block of a window whose size is not a multiple of the block, or a block
-  // that runs into padding) still loads its share of every chunk and meets
-  // the barriers, but forms no scores and no products
+  // that runs into padding) loads no Q and forms no scores and no products;
+  // it still loads its share of every chunk and meets the barriers
   const bool wave_real = __any(any_real);
+  if (wave_real) {
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+#pragma unroll
+      for (int s = 0; s < kS; ++s)
+        qop[u][s] = __builtin_bit_cast(bf16x8_t, ldg16(q + row_at(qtok[u], p.sq) + hoff + 32 * s + 8 * g4));
+  }
 
   // ---- chunk loader: thread tid moves 16-byte pieces tid + kThreads i of K and V
   // (key row tid / kCh + i kThreads / kCh, chunk tid % kCh). Chunk 0 maps its own
