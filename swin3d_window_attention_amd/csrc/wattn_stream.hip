@@ -311,28 +311,32 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   u32x4 ones8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   u32x2 ones4 = u32x2{0x3F803F80u, 0x3F803F80u};
 
+  // ---- a chunk of padding keys only (possible in a window that holds
+  // padding) adds nothing: their weights are exactly zero, so it is neither
+  // loaded nor computed. The test reads the chunk's codes in the ring, which
+  // were written at least one barrier earlier (workgroup-uniform: every wave
+  // reads the same codes) ----
+  auto all_pad = [&](int c) -> bool {
+    const uint8_t* cp = code_ring + (c % kRing) * kKC;
+    bool kp = true;
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) kp = kp && cp[kt * 16 + l16] == kPadSlot;
+    return __all(kp);
+  };
+  bool skip = kPad && cur.padded && all_pad(0);
   for (int c = 0; c < p.nchunk; ++c) {
     const int buf = c & 1;
     const uint8_t* kb = smem + buf * L::kBuf;
     const uint8_t* vb = kb + L::kTile;
     const uint8_t* cb = code_ring + (c % kRing) * kKC;
     const bool more = c + 1 < p.nchunk;
-    if (more) fetch(c + 1);  // next chunk in flight during this chunk's math
+    const bool skip_next = kPad && cur.padded && more && all_pad(c + 1);
+    if (more && !skip_next) fetch(c + 1);  // next chunk in flight during this chunk's math
     // chunks c + 4 .. c + 7 into the ring entries of chunks c - 4 .. c - 1,
     // whose last readers (the loads of chunk c - 1, the mask step of chunk
-    // c - 1) finished before the previous barrier
+    // c - 1, the padding test of chunk c) finished before the previous barrier
     if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
 
-    // ---- a chunk of padding keys only (possible in a window that holds
-    // padding) adds nothing: their weights are exactly zero, so it is skipped
-    // (wave-uniform: every wave reads the same codes) ----
-    bool skip = false;
-    if (kPad && cur.padded) {
-      bool kp = true;
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) kp = kp && cb[kt * 16 + l16] == kPadSlot;
-      skip = __all(kp);
-    }
     if (!skip && wave_real) {
       // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
       // for the wave's QT query tiles. Consecutive MFMAs take independent
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
 
     // ---- next chunk into the other buffer (everyone finished chunk c - 1,
     // the last reader of that buffer, at the previous barrier) ----
-    if (more) {
+    if (more && !skip_next) {
       uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
       clear_pad(c + 1);
 #pragma unroll
@@ -511,6 +515,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       }
     }
     __syncthreads();
+    skip = skip_next;
   }
 
   // ---- normalise and scatter (queries of the window only): tiles 2 m and
