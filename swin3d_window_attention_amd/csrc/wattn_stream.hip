@@ -324,198 +324,204 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
     return __all(kp);
   };
   bool skip = kPad && cur.padded && all_pad(0);
-  for (int c = 0; c < p.nchunk; ++c) {
-    const int buf = c & 1;
-    const uint8_t* kb = smem + buf * L::kBuf;
-    const uint8_t* vb = kb + L::kTile;
-    const uint8_t* cb = code_ring + (c % kRing) * kKC;
-    const bool more = c + 1 < p.nchunk;
-    const bool skip_next = kPad && cur.padded && more && all_pad(c + 1);
-    if (more && !skip_next) fetch(c + 1);  // next chunk in flight during this chunk's math
-    // chunks c + 4 .. c + 7 into the ring entries of chunks c - 4 .. c - 1,
-    // whose last readers (the loads of chunk c - 1, the mask step of chunk
-    // c - 1, the padding test of chunk c) finished before the previous barrier
-    if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
+  // the chunk loop runs two chunks per trip, so that the buffer of each is
+  // a compile-time constant (LDS offsets as immediates)
+  auto step = [&](int c, auto buf_) {
+      constexpr int buf = decltype(buf_)::value;  // = c & 1
+      const uint8_t* kb = smem + buf * L::kBuf;
+      const uint8_t* vb = kb + L::kTile;
+      const uint8_t* cb = code_ring + (c % kRing) * kKC;
+      const bool more = c + 1 < p.nchunk;
+      const bool skip_next = kPad && cur.padded && more && all_pad(c + 1);
+      if (more && !skip_next) fetch(c + 1);  // next chunk in flight during this chunk's math
+      // chunks c + 4 .. c + 7 into the ring entries of chunks c - 4 .. c - 1,
+      // whose last readers (the loads of chunk c - 1, the mask step of chunk
+      // c - 1, the padding test of chunk c) finished before the previous barrier
+      if (c % 4 == 0 && c + 4 < p.nchunk) fill_ring(c + 4);
 
-    if (!skip && wave_real) {
-      // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
-      // for the wave's QT query tiles. Consecutive MFMAs take independent
-      // accumulators: with fewer than four per k-step, even and odd k-steps
-      // accumulate separately, so that no MFMA takes its accumulator from one
-      // of the three before it ----
-      constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
-      // the wave's priority is raised while it issues matrix-core work, so
-      // that of the waves of a SIMD the one with products ready goes first
-      // and the others' vector work fills in behind it
-      __builtin_amdgcn_s_setprio(1);
-      floatx4 S2[kAcc][QT][kKT];
-#pragma unroll
-      for (int a = 0; a < kAcc; ++a)
-#pragma unroll
-        for (int u = 0; u < QT; ++u)
-#pragma unroll
-          for (int kt = 0; kt < kKT; ++kt) S2[a][u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        bf16x8_t kf[kKT];
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-          kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int u = 0; u < QT; ++u) {
-            ST_BEFORE(kf[kt]);
-            S2[s % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[u][s], S2[s % kAcc][u][kt], 0, 0, 0);
-            ST_AFTER(S2[s % kAcc][u][kt]);
-            ST_PIN_MFMA();
-          }
-      }
-      // mask k-step: the window has a cut or padding, or this chunk runs past N
-      if (cur.masked || (c + 1) * kKC > p.g.N) {
-        bf16x8_t xf[kKT];
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-          xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int u = 0; u < QT; ++u) {
-            ST_BEFORE(xf[kt]);
-            S2[kS % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb[u], S2[kS % kAcc][u][kt], 0, 0, 0);
-            ST_AFTER(S2[kS % kAcc][u][kt]);
-            ST_PIN_MFMA();
-          }
-      }
-
-      __builtin_amdgcn_s_setprio(0);
-      // ---- online softmax. The chunk maxima of all QT tiles first, then their
-      // lane exchanges side by side (each waits on the LDS crossbar once for
-      // all tiles), then the exponentials ----
-      bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
-      bf16x4_t Pt[QT];
-      floatx4 S[QT][kKT];
-      float mc[QT];
-#pragma unroll
-      for (int u = 0; u < QT; ++u) {
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) S[u][kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
-        // the chunk max, taken from the reference m on (the growth test below
-        // compares with m anyway); NaN-propagating maxima need no quieting of
-        // their inputs, which saves an instruction per operand the compiler
-        // cannot prove canonical
-        mc[u] = m[u];
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mc[u] = __builtin_elementwise_maximum(mc[u], S[u][kt][i]);
-      }
-      int xs[QT];
-#pragma unroll
-      for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc[u]), 0x401F);
-#pragma unroll
-      for (int u = 0; u < QT; ++u) mc[u] = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
-#pragma unroll
-      for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc[u]));
-#pragma unroll
-      for (int u = 0; u < QT; ++u) {
-        const float mc_w = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
-        // the reference max of a row moves only when the chunk's max exceeds it
-        // by more than kLazy in the exponent (always on the first chunk, where
-        // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
-        // does not depend on the reference
-        const bool grow = (mc_w - m[u]) * c2 > kLazy;
-        const float m_new = grow ? mc_w : m[u];
-        const float nm = -m_new * c2;
-        floatx4 P[kKT];
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[u][kt][i], c2, nm));
-        if (__any(grow)) {  // wave-uniform
-          const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
-          Ls[u][0] *= alpha;
-#pragma unroll
-          for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+      if (!skip && wave_real) {
+        // ---- S^T = K Q^T for this chunk's key tiles, each K operand read once
+        // for the wave's QT query tiles. Consecutive MFMAs take independent
+        // accumulators: with fewer than four per k-step, even and odd k-steps
+        // accumulate separately, so that no MFMA takes its accumulator from one
+        // of the three before it ----
+        constexpr int kAcc = kKT * QT >= 4 ? 1 : 2;
+        // the wave's priority is raised while it issues matrix-core work, so
+        // that of the waves of a SIMD the one with products ready goes first
+        // and the others' vector work fills in behind it
+        __builtin_amdgcn_s_setprio(1);
+        floatx4 S2[kAcc][QT][kKT];
+  #pragma unroll
+        for (int a = 0; a < kAcc; ++a)
+  #pragma unroll
+          for (int u = 0; u < QT; ++u)
+  #pragma unroll
+            for (int kt = 0; kt < kKT; ++kt) S2[a][u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int s = 0; s < kS; ++s) {
+          bf16x8_t kf[kKT];
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+            kf[kt] = *reinterpret_cast<const bf16x8_t*>(kb + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+  #pragma unroll
+            for (int u = 0; u < QT; ++u) {
+              ST_BEFORE(kf[kt]);
+              S2[s % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qop[u][s], S2[s % kAcc][u][kt], 0, 0, 0);
+              ST_AFTER(S2[s % kAcc][u][kt]);
+              ST_PIN_MFMA();
+            }
         }
-        m[u] = m_new;
-#pragma unroll
-        for (int j = 0; j < kJ; ++j)
-          Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
-                                             __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
-        Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
-      }
-
-      __builtin_amdgcn_s_setprio(1);
-      // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
-      // once for the wave's QT query tiles ----
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        u32x4 vf[kT];
-#pragma unroll
-        for (int t = 0; t < kT; ++t) {
-          const int d = dbase(t, qd);
-          const int lo_off = v_off<DH>(32 * j + 4 * g4 + e, d);
-          const int hi_off = v_off<DH>(32 * j + 16 + 4 * g4 + e, d);
-          const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
-          const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
-          vf[t] = u32x4{a[0], a[1], b[0], b[1]};
+        // mask k-step: the window has a cut or padding, or this chunk runs past N
+        if (cur.masked || (c + 1) * kKC > p.g.N) {
+          bf16x8_t xf[kKT];
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+            xf[kt] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (cb[kt * 16 + l16] * 4 + g4) * 16);
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+  #pragma unroll
+            for (int u = 0; u < QT; ++u) {
+              ST_BEFORE(xf[kt]);
+              S2[kS % kAcc][u][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kt], qxb[u], S2[kS % kAcc][u][kt], 0, 0, 0);
+              ST_AFTER(S2[kS % kAcc][u][kt]);
+              ST_PIN_MFMA();
+            }
         }
-#pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
-          for (int u = 0; u < QT; ++u) {
-            O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
-            ST_PIN_MFMA();
-          }
-#pragma unroll
+
+        __builtin_amdgcn_s_setprio(0);
+        // ---- online softmax. The chunk maxima of all QT tiles first, then their
+        // lane exchanges side by side (each waits on the LDS crossbar once for
+        // all tiles), then the exponentials ----
+        bf16x8_t Pb[QT][kJ > 0 ? kJ : 1];
+        bf16x4_t Pt[QT];
+        floatx4 S[QT][kKT];
+        float mc[QT];
+  #pragma unroll
         for (int u = 0; u < QT; ++u) {
-          ST_BEFORE(ones8);
-          Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[u][j], Ls[u], 0, 0, 0);
-          ST_AFTER(Ls[u]);
-          ST_PIN_MFMA();
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt) S[u][kt] = kAcc == 1 ? S2[0][u][kt] : S2[0][u][kt] + S2[kAcc - 1][u][kt];
+          // the chunk max, taken from the reference m on (the growth test below
+          // compares with m anyway); NaN-propagating maxima need no quieting of
+          // their inputs, which saves an instruction per operand the compiler
+          // cannot prove canonical
+          mc[u] = m[u];
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) mc[u] = __builtin_elementwise_maximum(mc[u], S[u][kt][i]);
         }
-      }
-      if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
-        short4_t vt[kT];
-#pragma unroll
-        for (int t = 0; t < kT; ++t) {
-          const int d = dbase(t, qd);
-          const int key = 32 * kJ + 4 * g4 + e;
-          vt[t] = lds_tr(vb, v_off<DH>(key, d));
+        int xs[QT];
+  #pragma unroll
+        for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mc[u]), 0x401F);
+  #pragma unroll
+        for (int u = 0; u < QT; ++u) mc[u] = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
+  #pragma unroll
+        for (int u = 0; u < QT; ++u) xs[u] = __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mc[u]));
+  #pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          const float mc_w = __builtin_elementwise_maximum(mc[u], __builtin_bit_cast(float, xs[u]));
+          // the reference max of a row moves only when the chunk's max exceeds it
+          // by more than kLazy in the exponent (always on the first chunk, where
+          // m = -inf), so P <= 2^kLazy and most chunks rescale nothing; softmax
+          // does not depend on the reference
+          const bool grow = (mc_w - m[u]) * c2 > kLazy;
+          const float m_new = grow ? mc_w : m[u];
+          const float nm = -m_new * c2;
+          floatx4 P[kKT];
+  #pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) P[kt][i] = __builtin_amdgcn_exp2f(fmaf(S[u][kt][i], c2, nm));
+          if (__any(grow)) {  // wave-uniform
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m[u] - m_new) * c2) : 1.0f;  // 0 on the first chunk
+            Ls[u][0] *= alpha;
+  #pragma unroll
+            for (int t = 0; t < kT; ++t) O[u][t] *= alpha;
+          }
+          m[u] = m_new;
+  #pragma unroll
+          for (int j = 0; j < kJ; ++j)
+            Pb[u][j] = __builtin_shufflevector(__builtin_convertvector(P[2 * j], bf16x4_t),
+                                               __builtin_convertvector(P[2 * j + 1], bf16x4_t), 0, 1, 2, 3, 4, 5, 6, 7);
+          Pt[u] = __builtin_convertvector(P[kKT - 1], bf16x4_t);  // 16-key step (kTail)
         }
-#pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
+
+        __builtin_amdgcn_s_setprio(1);
+        // ---- O^T += V^T P^T over the chunk's 32-key steps, each V operand read
+        // once for the wave's QT query tiles ----
+  #pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          u32x4 vf[kT];
+  #pragma unroll
+          for (int t = 0; t < kT; ++t) {
+            const int d = dbase(t, qd);
+            const int lo_off = v_off<DH>(32 * j + 4 * g4 + e, d);
+            const int hi_off = v_off<DH>(32 * j + 16 + 4 * g4 + e, d);
+            const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, lo_off));
+            const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, hi_off));
+            vf[t] = u32x4{a[0], a[1], b[0], b[1]};
+          }
+  #pragma unroll
+          for (int t = 0; t < kT; ++t)
+  #pragma unroll
+            for (int u = 0; u < QT; ++u) {
+              O[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[t]), Pb[u][j], O[u][t], 0, 0, 0);
+              ST_PIN_MFMA();
+            }
+  #pragma unroll
           for (int u = 0; u < QT; ++u) {
-            O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
+            ST_BEFORE(ones8);
+            Ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[u][j], Ls[u], 0, 0, 0);
+            ST_AFTER(Ls[u]);
             ST_PIN_MFMA();
           }
-#pragma unroll
-        for (int u = 0; u < QT; ++u) {
-          ST_BEFORE(ones4);
-          Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
-          ST_AFTER(Ls[u]);
-          ST_PIN_MFMA();
+        }
+        if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
+          short4_t vt[kT];
+  #pragma unroll
+          for (int t = 0; t < kT; ++t) {
+            const int d = dbase(t, qd);
+            const int key = 32 * kJ + 4 * g4 + e;
+            vt[t] = lds_tr(vb, v_off<DH>(key, d));
+          }
+  #pragma unroll
+          for (int t = 0; t < kT; ++t)
+  #pragma unroll
+            for (int u = 0; u < QT; ++u) {
+              O[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt[u]), O[u][t], 0, 0, 0);
+              ST_PIN_MFMA();
+            }
+  #pragma unroll
+          for (int u = 0; u < QT; ++u) {
+            ST_BEFORE(ones4);
+            Ls[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt[u]), Ls[u], 0, 0, 0);
+            ST_AFTER(Ls[u]);
+            ST_PIN_MFMA();
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+
+      // ---- next chunk into the other buffer (everyone finished chunk c - 1,
+      // the last reader of that buffer, at the previous barrier) ----
+      if (more && !skip_next) {
+        uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
+        clear_pad(c + 1);
+  #pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          const int r = my_row + (kThreads / kCh) * i;
+          *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, my_ch)) = kr[i];
+          *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, my_ch)) = vr[i];
         }
       }
-      __builtin_amdgcn_s_setprio(0);
-    }
-
-    // ---- next chunk into the other buffer (everyone finished chunk c - 1,
-    // the last reader of that buffer, at the previous barrier) ----
-    if (more && !skip_next) {
-      uint8_t* nb = smem + (buf ^ 1) * L::kBuf;
-      clear_pad(c + 1);
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int r = my_row + (kThreads / kCh) * i;
-        *reinterpret_cast<u32x4*>(nb + row_off<DH>(r, my_ch)) = kr[i];
-        *reinterpret_cast<u32x4*>(nb + L::kTile + row_off<DH>(r, my_ch)) = vr[i];
-      }
-    }
-    __syncthreads();
-    skip = skip_next;
+      __syncthreads();
+      skip = skip_next;
+  };
+  for (int c = 0; c < p.nchunk; c += 2) {
+    step(c, std::integral_constant<int, 0>{});
+    if (c + 1 < p.nchunk) step(c + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and scatter (queries of the window only): tiles 2 m and
