@@ -88,6 +88,10 @@ struct StreamParams {
   uint32_t sq, sk, sv, so;  // token strides of Q, K, V, O (elements, < 2^31)
   float c2;
   uint32_t beta01, beta2, pad;
+  // K and V token stride in bytes where both are addressed by a 32-bit byte
+  // offset from the head's column (equal strides, at most 2^24 tokens, every
+  // offset below 2^32); 0: 64-bit addresses
+  uint32_t kv2;
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
@@ -117,7 +121,7 @@ __device__ __forceinline__ int v_off(int key, int d) {
 }
 __device__ __forceinline__ int dbase(int t, int q) { return (t >> 1) * 32 + q * 8 + 4 * ((q ^ t) & 1); }
 
-template <int DH, int WAVES, int KC, int QT, bool kPad>
+template <int DH, int WAVES, int KC, int QT, bool kPad, bool kOff32>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 3 : 2))) void wattn_stream_item(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
@@ -200,6 +204,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
   const int my_row = tid / kCh, my_ch = tid % kCh;
   const uint16_t* kcol = k + hoff + 8 * my_ch;
   const uint16_t* vcol = v + hoff + 8 * my_ch;
+  const uint8_t* khead = reinterpret_cast<const uint8_t*>(k + hoff);  // workgroup-uniform bases
+  const uint8_t* vhead = reinterpret_cast<const uint8_t*>(v + hoff);
   // Padding slots (and slots past N) load a stand-in, token 0; their K and V
   // rows are replaced by zeros before they reach LDS, so the stand-in's values
   // never reach an output (an Inf or NaN in it stays in its own window). Ring
@@ -226,8 +232,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DH <
       t = pad ? 0 : t;
       // ordinary (not non-temporal) loads: the query blocks of a window read
       // the same K and V rows one after another on one XCD, from its L2
-      kr[i] = *reinterpret_cast<const u32x4*>(kcol + row_at(t, p.sk));
-      vr[i] = *reinterpret_cast<const u32x4*>(vcol + row_at(t, p.sv));
+      if constexpr (kOff32) {  // one 24-bit multiply-add per row, the same offset into K and V
+        const uint32_t off = __umul24((uint32_t)t, p.kv2) + 16u * (uint32_t)my_ch;
+        kr[i] = *reinterpret_cast<const u32x4*>(khead + off);
+        vr[i] = *reinterpret_cast<const u32x4*>(vhead + off);
+      } else {
+        kr[i] = *reinterpret_cast<const u32x4*>(kcol + row_at(t, p.sk));
+        vr[i] = *reinterpret_cast<const u32x4*>(vcol + row_at(t, p.sv));
+      }
     }
   };
   // zero the stand-in rows of chunk c (wave-uniform: only chunks of a window
@@ -871,6 +883,10 @@ StreamParams make_params(const swin3d_wattn_plan* pl, const swin3d_wattn_strides
   p.beta01 = (uint32_t)pl->beta_bf16[0] | ((uint32_t)pl->beta_bf16[1] << 16);
   p.beta2 = pl->beta_bf16[2];
   p.pad = pl->pad_bf16;
+  const int64_t dh2 = 2 * (int64_t)pl->desc.head_dim;
+  const bool off32 = st->k == st->v && pl->tokens <= (int64_t(1) << 24) && 2 * st->k < (int64_t(1) << 24) &&
+                     (pl->tokens - 1) * 2 * st->k + dh2 < (int64_t(1) << 32);
+  p.kv2 = off32 ? (uint32_t)(2 * st->k) : 0u;
   return p;
 }
 
@@ -888,9 +904,13 @@ hipError_t launch(const swin3d_wattn_plan* pl, const void* q, const void* k, con
   // grids that need padding get the instance that skips query blocks and key
   // chunks of padding only
   const bool pad = pl->padded[0] != pl->desc.D || pl->padded[1] != pl->desc.H || pl->padded[2] != pl->desc.W;
-  return hipLaunchKernel(pad ? reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, true>)
-                             : reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, false>),
-                         grid, dim3(64 * WAVES), args, 0, s);
+  // and K/V within 32-bit byte offsets the instance with one multiply-add
+  // per loaded row
+  const void* fn = p.kv2 ? (pad ? reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, true, true>)
+                                : reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, false, true>))
+                         : (pad ? reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, true, false>)
+                                : reinterpret_cast<const void*>(&wattn_stream_item<DH, WAVES, KC, QT, false, false>));
+  return hipLaunchKernel(fn, grid, dim3(64 * WAVES), args, 0, s);
 }
 
 template <int DH, int NT>
