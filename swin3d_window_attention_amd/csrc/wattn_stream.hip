@@ -737,6 +737,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // set for all tiles (the empty asm before each use pins the order)
   u32x4 ones8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   u32x2 ones4 = u32x2{0x3F803F80u, 0x3F803F80u};
+  // region codes of this lane's key slots kt 16 + l16 (windows with a cut or
+  // padding), four bits each, eight to a register: the mask k-step finds
+  // each key's feature without a dependent LDS read
+  constexpr int kCW = (NT + 7) / 8;
+  uint32_t kcodes[kCW];
+#pragma unroll
+  for (int w = 0; w < kCW; ++w) kcodes[w] = 0;
+  if (cur.masked) {
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) kcodes[kt / 8] |= (uint32_t)codeS[kt * 16 + l16] << (4 * (kt % 8));
+  }
+  auto tiles = [&](auto mask_) {
+  constexpr bool kMask = decltype(mask_)::value;
 #pragma unroll
   for (int i = 0; i < kMaxQT; ++i) {
     const int qt = wave + kWaves * i;
@@ -749,34 +762,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
     {
+      // one stream of MFMAs: the Q K^T k-steps (k-step idx / NT of key tile
+      // idx % NT), then in windows with a cut or padding the mask k-step of
+      // every key tile; A operands (K, or the key's mask feature located by
+      // its code) read kAhead MFMAs ahead
       constexpr int kSteps = kS * NT;
+      constexpr int kAll = kSteps + (kMask ? NT : 0);
       constexpr int kAhead = 8;
-      bf16x8_t kf[kSteps];
+      const bf16x8_t qxb =
+          kMask ? *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (36 + qcode[i] * 4 + g4) * 16) : bf16x8_t{};
+      bf16x8_t kf[kAll];
       auto kread = [&](int idx) {
-        const int s = idx / NT, kt = idx % NT;
-        kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+        if (idx < kSteps) {
+          const int s = idx / NT, kt = idx % NT;
+          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+        } else {
+          const int kt = idx - kSteps;
+          const uint32_t code = (kcodes[kt / 8] >> (4 * (kt % 8))) & 15u;
+          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (code * 4 + g4) * 16);
+        }
       };
 #pragma unroll
       for (int idx = 0; idx < kAhead; ++idx) kread(idx);
 #pragma unroll
-      for (int idx = 0; idx < kSteps; ++idx) {
-        const int s = idx / NT, kt = idx % NT;
+      for (int idx = 0; idx < kAll; ++idx) {
+        const int kt = idx < kSteps ? idx % NT : idx - kSteps;
         ST_BEFORE(kf[idx]);
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], qop[i][s], S[kt], 0, 0, 0);
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], idx < kSteps ? qop[i][idx / NT] : qxb, S[kt], 0, 0, 0);
         ST_AFTER(S[kt]);
         ST_PIN_MFMA_LDS();
-        if (idx + kAhead < kSteps) kread(idx + kAhead);
-      }
-    }
-    if (cur.masked) {
-      const bf16x8_t qxb = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (36 + qcode[i] * 4 + g4) * 16);
-#pragma unroll
-      for (int kt = 0; kt < NT; ++kt) {
-        bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (codeS[kt * 16 + l16] * 4 + g4) * 16);
-        ST_BEFORE(xf);
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, qxb, S[kt], 0, 0, 0);
-        ST_AFTER(S[kt]);
-        ST_PIN_MFMA();
+        if (idx + kAhead < kAll) kread(idx + kAhead);
       }
     }
 
@@ -865,6 +880,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       }
     }
   }
+  };
+  if (cur.masked)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
 }
 
 // kernel parameters of a plan: nqb query blocks and nchunk key chunks per window
