@@ -749,137 +749,137 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int kt = 0; kt < NT; ++kt) kcodes[kt / 8] |= (uint32_t)codeS[kt * 16 + l16] << (4 * (kt % 8));
   }
   auto tiles = [&](auto mask_) {
-  constexpr bool kMask = decltype(mask_)::value;
+    constexpr bool kMask = decltype(mask_)::value;
 #pragma unroll
-  for (int i = 0; i < kMaxQT; ++i) {
-    const int qt = wave + kWaves * i;
-    if (qt >= NT) break;
+    for (int i = 0; i < kMaxQT; ++i) {
+      const int qt = wave + kWaves * i;
+      if (qt >= NT) break;
 
-    // ---- S^T = K Q^T over all key tiles; K operands read kAhead MFMAs ahead.
-    // k-step s of key tile kt is MFMA s NT + kt, so an accumulator's
-    // successive MFMAs lie NT >= 4 apart ----
-    floatx4 S[NT];
+      // ---- S^T = K Q^T over all key tiles; K operands read kAhead MFMAs ahead.
+      // k-step s of key tile kt is MFMA s NT + kt, so an accumulator's
+      // successive MFMAs lie NT >= 4 apart ----
+      floatx4 S[NT];
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    {
-      // one stream of MFMAs: the Q K^T k-steps (k-step idx / NT of key tile
-      // idx % NT), then in windows with a cut or padding the mask k-step of
-      // every key tile; A operands (K, or the key's mask feature located by
-      // its code) read kAhead MFMAs ahead
-      constexpr int kSteps = kS * NT;
-      constexpr int kAll = kSteps + (kMask ? NT : 0);
-      constexpr int kAhead = 8;
-      const bf16x8_t qxb =
-          kMask ? *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (36 + qcode[i] * 4 + g4) * 16) : bf16x8_t{};
-      bf16x8_t kf[kAll];
-      auto kread = [&](int idx) {
-        if (idx < kSteps) {
-          const int s = idx / NT, kt = idx % NT;
-          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + row_off<DH>(kt * 16 + l16, 4 * s + g4));
-        } else {
-          const int kt = idx - kSteps;
-          const uint32_t code = (kcodes[kt / 8] >> (4 * (kt % 8))) & 15u;
-          kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (code * 4 + g4) * 16);
+      for (int kt = 0; kt < NT; ++kt) S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      {
+        // one stream of MFMAs: the Q K^T k-steps (k-step idx / NT of key tile
+        // idx % NT), then in windows with a cut or padding the mask k-step of
+        // every key tile; A operands (K, or the key's mask feature located by
+        // its code) read kAhead MFMAs ahead
+        constexpr int kSteps = kS * NT;
+        constexpr int kAll = kSteps + (kMask ? NT : 0);
+        constexpr int kAhead = 8;
+        const bf16x8_t qxb =
+            kMask ? *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (36 + qcode[i] * 4 + g4) * 16) : bf16x8_t{};
+        bf16x8_t kf[kAll];
+        auto kread = [&](int idx) {
+          if (idx < kSteps) {
+            const int s = idx / NT, kt = idx % NT;
+            kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + row_off<DH>(kt * 16 + l16, 4 * s + g4));
+          } else {
+            const int kt = idx - kSteps;
+            const uint32_t code = (kcodes[kt / 8] >> (4 * (kt % 8))) & 15u;
+            kf[idx] = *reinterpret_cast<const bf16x8_t*>(smem + L::kXt + (code * 4 + g4) * 16);
+          }
+        };
+#pragma unroll
+        for (int idx = 0; idx < kAhead; ++idx) kread(idx);
+#pragma unroll
+        for (int idx = 0; idx < kAll; ++idx) {
+          const int kt = idx < kSteps ? idx % NT : idx - kSteps;
+          ST_BEFORE(kf[idx]);
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], idx < kSteps ? qop[i][idx / NT] : qxb, S[kt], 0, 0, 0);
+          ST_AFTER(S[kt]);
+          ST_PIN_MFMA_LDS();
+          if (idx + kAhead < kAll) kread(idx + kAhead);
+        }
+      }
+
+      // ---- softmax in FP32 (log2 domain), P to bf16 in the B-operand layout;
+      // NaN-propagating maxima need no quieting of their inputs ----
+      float mx = S[0][0];
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = __builtin_elementwise_maximum(mx, S[kt][r]);
+      mx = __builtin_elementwise_maximum(
+          mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
+      mx = __builtin_elementwise_maximum(
+          mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mx))));
+      const float nm = -mx * c2;
+      bf16x8_t Pb[kJ > 0 ? kJ : 1];
+      bf16x4_t Pt, prev;
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) {
+        floatx4 P;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], c2, nm));
+        const bf16x4_t pb = __builtin_convertvector(P, bf16x4_t);
+        if (kt & 1)
+          Pb[kt / 2] = __builtin_shufflevector(prev, pb, 0, 1, 2, 3, 4, 5, 6, 7);  // keys 32 (kt / 2) ..
+        else if (kt / 2 < kJ)
+          prev = pb;
+        else
+          Pt = pb;  // the 16-key step (kTail)
+      }
+
+      // ---- O^T = V^T P^T: V operands of step j + 1 read during step j; the
+      // row sums of the same bf16 P from the matrix core (ones x P^T) ----
+      floatx4 O[kT], Ls = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      u32x4 vf[2][kT];
+      auto vread = [&](int j, int buf) {
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          const int d = dbase(t, qd);
+          const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 4 * g4 + e, d)));
+          const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 16 + 4 * g4 + e, d)));
+          vf[buf][t] = u32x4{a[0], a[1], b[0], b[1]};
         }
       };
+      vread(0, 0);
 #pragma unroll
-      for (int idx = 0; idx < kAhead; ++idx) kread(idx);
+      for (int j = 0; j < kJ; ++j) {
+        if (j + 1 < kJ) vread(j + 1, (j + 1) & 1);
 #pragma unroll
-      for (int idx = 0; idx < kAll; ++idx) {
-        const int kt = idx < kSteps ? idx % NT : idx - kSteps;
-        ST_BEFORE(kf[idx]);
-        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[idx], idx < kSteps ? qop[i][idx / NT] : qxb, S[kt], 0, 0, 0);
-        ST_AFTER(S[kt]);
-        ST_PIN_MFMA_LDS();
-        if (idx + kAhead < kAll) kread(idx + kAhead);
-      }
-    }
-
-    // ---- softmax in FP32 (log2 domain), P to bf16 in the B-operand layout;
-    // NaN-propagating maxima need no quieting of their inputs ----
-    float mx = S[0][0];
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = __builtin_elementwise_maximum(mx, S[kt][r]);
-    mx = __builtin_elementwise_maximum(
-        mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
-    mx = __builtin_elementwise_maximum(
-        mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, mx))));
-    const float nm = -mx * c2;
-    bf16x8_t Pb[kJ > 0 ? kJ : 1];
-    bf16x4_t Pt, prev;
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
-      floatx4 P;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) P[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], c2, nm));
-      const bf16x4_t pb = __builtin_convertvector(P, bf16x4_t);
-      if (kt & 1)
-        Pb[kt / 2] = __builtin_shufflevector(prev, pb, 0, 1, 2, 3, 4, 5, 6, 7);  // keys 32 (kt / 2) ..
-      else if (kt / 2 < kJ)
-        prev = pb;
-      else
-        Pt = pb;  // the 16-key step (kTail)
-    }
-
-    // ---- O^T = V^T P^T: V operands of step j + 1 read during step j; the
-    // row sums of the same bf16 P from the matrix core (ones x P^T) ----
-    floatx4 O[kT], Ls = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < kT; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    u32x4 vf[2][kT];
-    auto vread = [&](int j, int buf) {
-#pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        const int d = dbase(t, qd);
-        const u32x2 a = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 4 * g4 + e, d)));
-        const u32x2 b = __builtin_bit_cast(u32x2, lds_tr(vb, v_off<DH>(32 * j + 16 + 4 * g4 + e, d)));
-        vf[buf][t] = u32x4{a[0], a[1], b[0], b[1]};
-      }
-    };
-    vread(0, 0);
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      if (j + 1 < kJ) vread(j + 1, (j + 1) & 1);
-#pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
+        for (int t = 0; t < kT; ++t) {
+          O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[j & 1][t]), Pb[j], O[t], 0, 0, 0);
+          ST_PIN_MFMA_LDS();
+        }
+        ST_BEFORE(ones8);
+        Ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[j], Ls, 0, 0, 0);
+        ST_AFTER(Ls);
         ST_PIN_MFMA_LDS();
       }
-      ST_BEFORE(ones8);
-      Ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones8), Pb[j], Ls, 0, 0, 0);
-      ST_AFTER(Ls);
-      ST_PIN_MFMA_LDS();
-    }
-    if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
-      short4_t vt[kT];
+      if (kTail) {  // keys 32 kJ .. 32 kJ + 15: v_mfma_f32_16x16x16_bf16
+        short4_t vt[kT];
 #pragma unroll
-      for (int t = 0; t < kT; ++t) vt[t] = lds_tr(vb, v_off<DH>(32 * kJ + 4 * g4 + e, dbase(t, qd)));
+        for (int t = 0; t < kT; ++t) vt[t] = lds_tr(vb, v_off<DH>(32 * kJ + 4 * g4 + e, dbase(t, qd)));
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
+        for (int t = 0; t < kT; ++t) {
+          O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[t], __builtin_bit_cast(short4_t, Pt), O[t], 0, 0, 0);
+          ST_PIN_MFMA();
+        }
+        ST_BEFORE(ones4);
+        Ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt), Ls, 0, 0, 0);
+        ST_AFTER(Ls);
         ST_PIN_MFMA();
       }
-      ST_BEFORE(ones4);
-      Ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, ones4), __builtin_bit_cast(short4_t, Pt), Ls, 0, 0, 0);
-      ST_AFTER(Ls);
-      ST_PIN_MFMA();
-    }
-    const float inv = 1.0f / Ls[0];
+      const float inv = 1.0f / Ls[0];
 
-    // ---- normalise and scatter: one 16-byte store per pair of output tiles ----
-    if (qcode[i] != kPadSlot) {
-      uint16_t* out = o + row_at(qtok[i], p.so) + hoff;
+      // ---- normalise and scatter: one 16-byte store per pair of output tiles ----
+      if (qcode[i] != kPadSlot) {
+        uint16_t* out = o + row_at(qtok[i], p.so) + hoff;
 #pragma unroll
-      for (int m2 = 0; m2 < kT / 2; ++m2) {
-        const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
-        const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2 + 1] * inv, bf16x4_t));
-        const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
-        *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
+        for (int m2 = 0; m2 < kT / 2; ++m2) {
+          const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2] * inv, bf16x4_t));
+          const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[2 * m2 + 1] * inv, bf16x4_t));
+          const u32x4 w = odd ? u32x4{b[0], b[1], a[0], a[1]} : u32x4{a[0], a[1], b[0], b[1]};
+          *reinterpret_cast<u32x4*>(out + 32 * m2 + 8 * g4) = w;
+        }
       }
     }
-  }
   };
   if (cur.masked)
     tiles(std::true_type{});
