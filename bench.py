@@ -405,6 +405,36 @@ def warm_then_time(torch, run, stream, steps: int, warmup: int, warmup_ms: float
     return start.elapsed_time(end) / steps, extra
 
 
+ROTATE_OUTPUTS = 8           # output buffers cycled by output_rotation()
+ROTATE_MAX_BYTES = 1 << 30   # larger outputs already exceed the Infinity Cache many times over
+
+
+def output_rotation(torch, wl, run_into, like, stream, steps: int, warmup: int):
+    """Context for a timed workload: the same launches, but each writes the next of ROTATE_OUTPUTS
+    output buffers (8 x the output, well beyond the 256 MB Infinity Cache). Back-to-back launches
+    into one output buffer find much of the previous launch's output still in that cache, and
+    rewrite those lines there before they are ever written back to HBM; here every launch's output
+    reaches HBM, as it does for an output that goes to fresh memory. None for outputs above
+    ROTATE_MAX_BYTES (whose launches already write back all but a cache's worth)."""
+    out_bytes = like.numel() * like.element_size()
+    if out_bytes > ROTATE_MAX_BYTES:
+        return None
+    outs = [torch.empty_like(like) for _ in range(ROTATE_OUTPUTS)]
+    i = [0]
+
+    def run():
+        run_into(outs[i[0] % ROTATE_OUTPUTS])
+        i[0] += 1
+
+    ms, _ = warm_then_time(torch, run, stream, steps, max(warmup, ROTATE_OUTPUTS), 100.0)
+    del outs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    r = roofline_of(wl, ms)
+    return {"buffers": ROTATE_OUTPUTS, "bytes_per_buffer": out_bytes, "us_per_step": ms * 1e3,
+            "tokens_per_s": wl.tokens / (ms / 1e3), "roofline": r}
+
+
 def roofline_of(wl, ms: float) -> dict:
     """Position of one launch of workload wl taking ms against the bound of its kernel: HBM bytes
     at 8 TB/s or products at the matrix-core peak of their own type, whichever takes longer."""
@@ -436,6 +466,8 @@ def bench_configs(torch, dev, stream, args, names=CONFIG_WORKLOADS) -> dict:
         info = plan.info()
         ms, _ = warm_then_time(torch, lambda: plan.run(x["q"], x["k"], x["v"], o), stream, args.steps,
                                args.warmup, min(args.warmup_ms, 200.0))
+        rot = output_rotation(torch, wl, lambda oo: plan.run(x["q"], x["k"], x["v"], oo), o, stream, args.steps,
+                              args.warmup)
         nbytes, flops, nwin = algorithmic_work(wl)
         out[name] = {
             "shape": {"B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
@@ -447,6 +479,7 @@ def bench_configs(torch, dev, stream, args, names=CONFIG_WORKLOADS) -> dict:
             "algorithmic_bytes_per_launch": nbytes,
             "algorithmic_flops_per_launch": flops,
             "roofline": roofline_of(wl, ms),
+            "output_rotation": rot,
         }
         log(f"[bench] config {name}: {ms * 1e3:.1f} us per step, "
             f"{out[name]['roofline']['frac']:.3f} of the {out[name]['roofline']['bound']} roofline")
@@ -564,6 +597,8 @@ def main():
     for _ in range(2):
         plan.run(x["q"], x["k"], x["v"], o)
     pages_mean5 = sum(single_launches(5)) / 5
+    rotation = None if args.cold else output_rotation(
+        torch, wl, lambda oo: plan.run(x["q"], x["k"], x["v"], oo), o, stream, args.steps, args.warmup)
     copy_gbs = device_copy_gbs(torch, 1 << 29)
 
     configs = None
@@ -631,6 +666,7 @@ def main():
                              "mean_of_5_after_2_warmups": pages_mean5},
         "device_copy": {"gbs_read_plus_write": copy_gbs, "bytes": 1 << 29,
                         "algorithmic_frac_of_copy": gbs / copy_gbs},
+        "output_rotation": rotation,
         "algorithmic_bytes_per_launch": nbytes,
         "algorithmic_flops_per_launch": flops,
         "cpu_baseline": cpu,
