@@ -466,8 +466,8 @@ def bench_configs(torch, dev, stream, args, names=CONFIG_WORKLOADS) -> dict:
         info = plan.info()
         ms, _ = warm_then_time(torch, lambda: plan.run(x["q"], x["k"], x["v"], o), stream, args.steps,
                                args.warmup, min(args.warmup_ms, 200.0))
-        rot = output_rotation(torch, wl, lambda oo: plan.run(x["q"], x["k"], x["v"], oo), o, stream, args.steps,
-                              args.warmup)
+        rot = None if args.no_output_rotation else output_rotation(
+            torch, wl, lambda oo: plan.run(x["q"], x["k"], x["v"], oo), o, stream, args.steps, args.warmup)
         nbytes, flops, nwin = algorithmic_work(wl)
         out[name] = {
             "shape": {"B": wl.B, "grid": [wl.D, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
@@ -509,6 +509,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="with the headline workload: skip timing the other shapes (" +
                          ", ".join(CONFIG_WORKLOADS) + ") that the line reports under 'configs'")
+    ap.add_argument("--no-output-rotation", action="store_true",
+                    help="skip the output_rotation context (the same launches writing eight output buffers "
+                         "in turn), e.g. so that a profiler's kernel statistics hold the timed protocol only")
     ap.add_argument("--cold", action="store_true",
                     help="flush the 256 MB Infinity Cache (read a 1 GiB buffer) before every timed "
                          "launch and time each launch with its own events")
@@ -597,7 +600,7 @@ def main():
     for _ in range(2):
         plan.run(x["q"], x["k"], x["v"], o)
     pages_mean5 = sum(single_launches(5)) / 5
-    rotation = None if args.cold else output_rotation(
+    rotation = None if args.cold or args.no_output_rotation else output_rotation(
         torch, wl, lambda oo: plan.run(x["q"], x["k"], x["v"], oo), o, stream, args.steps, args.warmup)
     copy_gbs = device_copy_gbs(torch, 1 << 29)
 
