@@ -364,6 +364,24 @@ def bench_adaln(args):
     n = wl.B * wl.rows * wl.C
     nbytes = n * (elt[wl.x_dtype] + elt[wl.res_dtype] + elt[wl.out_dtype]) + 2 * wl.B * wl.C * 4
     gbs = nbytes / (ms / 1e3) / 1e9
+    # context: the same launches writing ROTATE_OUTPUTS output buffers in turn (see output_rotation)
+    rotation = None
+    out_bytes = out.numel() * out.element_size()
+    if not args.no_output_rotation and out_bytes <= ROTATE_MAX_BYTES:
+        outs = [torch.empty_like(out) for _ in range(ROTATE_OUTPUTS)]
+        i = [0]
+
+        def run_rot():
+            sw.adaln_residual(x, res, g, b, wl.eps, out=outs[i[0] % ROTATE_OUTPUTS])
+            i[0] += 1
+
+        rms, _ = warm_then_time(torch, run_rot, stream, args.steps, max(args.warmup, ROTATE_OUTPUTS), 100.0)
+        del outs
+        rg = nbytes / (rms / 1e3) / 1e9
+        rotation = {"buffers": ROTATE_OUTPUTS, "bytes_per_buffer": out_bytes, "us_per_step": rms * 1e3,
+                    "tokens_per_s": wl.B * wl.rows / (rms / 1e3),
+                    "roofline": {"bound": "hbm", "achieved": rg, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": rg / HBM_PEAK_GBS}}
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
@@ -377,7 +395,7 @@ def bench_adaln(args):
         "config": {"workload": wl.name, "B": wl.B, "rows": wl.rows, "C": wl.C, "eps": wl.eps},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes_per_launch": nbytes, "cpu_baseline": cpu,
+        "output_rotation": rotation, "algorithmic_bytes_per_launch": nbytes, "cpu_baseline": cpu,
     }), flush=True)
 
 
