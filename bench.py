@@ -424,7 +424,7 @@ def warm_then_time(torch, run, stream, steps: int, warmup: int, warmup_ms: float
 
 
 ROTATE_OUTPUTS = 8           # output buffers cycled by output_rotation()
-ROTATE_MAX_BYTES = 1 << 30   # larger outputs already exceed the Infinity Cache many times over
+ROTATE_MAX_BYTES = 1 << 30   # larger outputs exceed the 256 MB Infinity Cache at least four times over
 
 
 def output_rotation(torch, wl, run_into, like, stream, steps: int, warmup: int):
